@@ -1,0 +1,270 @@
+"""Benchmark of the static KV-cache decode path on one MI355X.
+
+One step = one decode step of the Llama-3-8B-shaped GQA stack: for each of
+the 32 layers, the in-place append of the new token's K/V at cache_index
+(kvc_append) and single-query attention of all 32 query heads over each
+sequence's valid rows (kvc_decode_attn). Batch 16, H_kv = 8, d_h = 128,
+max_context 4096, per-sequence valid_len ~ U[1024, 4096] (seeded), bf16
+storage with fp32 accumulation. All inputs are resident in HBM before the
+timed region; the step replays the same position (idempotent append) so
+every step moves the same bytes. The 32 layers occupy 8 GiB, far above the
+256 MB Infinity Cache, so rotating through them streams from HBM.
+
+Reported (one JSON line on stdout):
+  value        KV GB/s = KV bytes read per step / step time (graph-replayed)
+  roofline     the decode kernel: algorithmic bytes per launch / its mean
+               duration from HIP events on its stream, against 8 TB/s
+  cpu_baseline the float64 oracle timed on a bounded sample on the host
+
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-attention KV GB/s and % HBM peak; decode steps/s per layer at 1 GPU"
+HBM_PEAK_GBS = 8000.0
+WORKLOAD = "llama3_8b_gqa_bf16"
+KERNEL_SRC = os.path.join(ROOT, "static_kv_cache_amd", "csrc", "kvc_decode.hip")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "gqa_decode_llama3_8b_pmc.txt")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-repeats", type=int, default=20)
+    p.add_argument("--eager-only", action="store_true", help="skip the graph-replay leg")
+    p.add_argument("--workgroups", type=int, default=0,
+                   help="force the persistent attention grid size (0 = device default)")
+    return p.parse_args()
+
+
+def kernel_sha():
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def read_pmc_traffic():
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel source; else None."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    kv = {}
+    for line in open(PMC_SUMMARY):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != kernel_sha():
+        return None
+    try:
+        return int(float(kv["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+class Workload:
+    """Llama-3-8B-shaped decode stack resident on the GPU."""
+
+    def __init__(self, torch, dev):
+        from static_kv_cache_amd import kvc, synthetic
+        self.torch, self.kvc = torch, kvc
+        cfg = synthetic.WORKLOADS[WORKLOAD]
+        self.cfg = cfg
+        L, B, H, Hkv, D, S = (cfg["n_layers"], cfg["batch"], cfg["n_heads"], cfg["n_kv_heads"],
+                              cfg["head_dim"], cfg["max_context"])
+        self.L, self.B, self.H, self.Hkv, self.D, self.S = L, B, H, Hkv, D, S
+        self.cache = kvc.Cache(kvc.gqa_desc(L, B, H, Hkv, D, S, "bf16"))
+        c = synthetic.gqa_layer(cfg, seed_offset=0)
+        self.host = c
+        k = kvc.to_device(c["k_fill"], dev)
+        v = kvc.to_device(c["v_fill"], dev)
+        self.fill_bytes = 2 * k.numel() * k.element_size()
+        for layer in range(L):
+            self.cache.prefill_fill(layer, k, v, 0)
+        del k, v
+        rng = np.random.default_rng(cfg["seed"] + 7)
+        self.q = [kvc.to_device(synthetic.draw(rng, (B, H, D), "bf16"), dev) for _ in range(L)]
+        self.kn = [kvc.to_device(synthetic.draw(rng, (B, Hkv, 1, D), "bf16"), dev) for _ in range(L)]
+        self.vn = [kvc.to_device(synthetic.draw(rng, (B, Hkv, 1, D), "bf16"), dev) for _ in range(L)]
+        self.out = [torch.empty((B, H, D), dtype=torch.bfloat16, device=dev) for _ in range(L)]
+        self.valid = kvc.to_device(c["valid_lens"], dev)
+        self.ci = kvc.to_device(c["cache_index"], dev)
+        self.sm_scale = c["sm_scale"]
+        self.sum_valid = int(c["valid_lens"].sum())
+        torch.cuda.synchronize()
+        self.cache.check()
+        # bytes
+        p = 2
+        self.kv_read_per_layer = self.sum_valid * 2 * Hkv * D * p
+        self.decode_alg_bytes = (self.kv_read_per_layer + 2 * B * H * D * p + 8 * B)
+        self.append_bytes = 2 * (2 * B * Hkv * D * p) + 4 * B   # read + write of the new rows
+
+    def layer_step(self, layer, ev=None):
+        self.cache.append(layer, self.kn[layer], self.vn[layer], self.ci)
+        if ev is not None:
+            ev[0].record()
+        self.cache.decode_attn(layer, self.q[layer], self.out[layer], valid_lens=self.valid,
+                               cache_index=self.ci, sm_scale=self.sm_scale)
+        if ev is not None:
+            ev[1].record()
+
+    def step(self):
+        for layer in range(self.L):
+            self.layer_step(layer)
+
+
+def time_steps(torch, fn, steps):
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(steps):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / steps   # ms per step
+
+
+def cpu_baseline(wl, repeats):
+    """The oracle (float64 numpy, as it stands) on one full layer-step of the
+    same workload: append into the buffer model, then decode attention for
+    all 16 sequences x 32 heads, repeated `repeats` times."""
+    import oracle.attention as oatt
+    from oracle.buffer import RefCache
+    c = wl.host
+    ref = RefCache(1, wl.B, wl.Hkv, wl.S, wl.D, "bf16")
+    ref.fill(0, c["k_fill"], c["v_fill"], 0)
+    q = c["q"]
+    times = []
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        ref.append(0, c["k_new"], c["v_new"], c["cache_index"])
+        oatt.decode_attention(q, ref.keys(0), ref.values(0), c["valid_lens"], c["sm_scale"])
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times))
+    threads = 1
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+    except Exception:
+        pass
+    return dict(value=round(wl.kv_read_per_layer / t / 1e9, 4), unit="GB/s", cores=int(threads),
+                kind="oracle",
+                sample=(f"one layer-step (append + decode of all {wl.B} sequences x {wl.H} heads, "
+                        f"sum valid_len {wl.sum_valid}) of the same workload, median of {repeats}; "
+                        f"{t:.2f} s per layer-step = {1.0 / t:.4f} layer-steps/s; host has "
+                        f"{os.cpu_count()} logical CPUs"))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              f"sharding across GPUs is designed but not built", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"bench: setting up {WORKLOAD}")
+    wl = Workload(torch, dev)
+    if args.workgroups:
+        wl.cache.set_workgroups(args.workgroups)
+    log(f"bench: workgroups {wl.cache.workgroups()}, sum valid {wl.sum_valid}, "
+        f"KV bytes per layer {wl.kv_read_per_layer}")
+
+    # --- eager launches -------------------------------------------------
+    for _ in range(args.warmup):
+        wl.step()
+    ms_eager = time_steps(torch, wl.step, args.steps)
+    log(f"bench: eager {ms_eager:.4f} ms/step")
+
+    # --- per-kernel durations of the decode kernel (HIP events on its stream)
+    L = wl.L
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(L * args.steps)]
+    torch.cuda.synchronize()
+    for s in range(args.steps):
+        for layer in range(L):
+            wl.layer_step(layer, evs[s * L + layer])
+    torch.cuda.synchronize()
+    durs = [a.elapsed_time(b) for a, b in evs]
+    decode_ms = float(np.mean(durs))
+    log(f"bench: decode kernel mean {decode_ms * 1e3:.2f} us over {len(durs)} launches "
+        f"(median {np.median(durs) * 1e3:.2f})")
+
+    # --- graph replay of the whole step ---------------------------------
+    ms_graph = None
+    if not args.eager_only:
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            wl.step()        # one eager pass on the capture stream
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            wl.step()
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            g.replay()
+        ms_graph = time_steps(torch, g.replay, args.steps)
+        log(f"bench: graph {ms_graph:.4f} ms/step")
+    wl.cache.check()
+
+    ms = ms_graph if ms_graph is not None else ms_eager
+    kv_bytes_step = wl.kv_read_per_layer * L
+    value = kv_bytes_step / (ms * 1e-3) / 1e9
+    achieved = wl.decode_alg_bytes / (decode_ms * 1e-3) / 1e9
+    roof = dict(bound="hbm", achieved=round(achieved, 2), peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=round(achieved / HBM_PEAK_GBS, 4), traffic=read_pmc_traffic(),
+                kernel="gqa_decode_kernel<bf16,128,4>",
+                alg_bytes_per_launch=wl.decode_alg_bytes, mean_launch_us=round(decode_ms * 1e3, 3))
+    cpu = None if args.no_cpu_baseline else cpu_baseline(wl, args.cpu_repeats)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4),
+        "layer_steps_per_s": round(L / (ms * 1e-3), 1),
+        "decode_steps_per_s": round(1.0 / (ms * 1e-3), 2),
+        "eager_ms_per_step": round(ms_eager, 5),
+        "config": {"workload": WORKLOAD, "n_layers": L, "batch": wl.B, "n_heads": wl.H,
+                   "n_kv_heads": wl.Hkv, "head_dim": wl.D, "max_context": wl.S,
+                   "valid_len": "U[1024,4096] seed 2", "sum_valid_len": wl.sum_valid,
+                   "workgroups": wl.cache.workgroups()[0] or "resident",
+                   "launch": "hipgraph" if ms_graph is not None else "eager",
+                   "step": "32 x (append + decode attention)"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    wl.cache.free()
+
+
+if __name__ == "__main__":
+    main()

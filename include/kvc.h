@@ -1,0 +1,203 @@
+/*
+ * kvc.h -- C ABI of the static KV-cache decode library (libkvc.so, gfx950).
+ *
+ * The library implements autoregressive decode over a KV cache that is
+ * allocated once, at its full capacity, per layer:
+ *
+ *   - "KV-Cache Mechanics" (DantinoX docs), "AR Static KV-Cache": one
+ *     [B, H_kv, max_context, head_size] array per layer, allocated up front so
+ *     shapes never change between decode steps; prefill writes from
+ *     cache_index 0, each decode step writes at cache_index.
+ *   - "KV Cache Optimization: GQA Audit, In-Place Buffers, Persistent
+ *     Prompts", "#2 In-place KV cache updates": new rows are slice-assigned
+ *     into the fixed buffer (no concat, no regrowth); reads stop at the valid
+ *     length.
+ *   - "10.3 - KV cache implementation details", section 5: per layer, append
+ *     the new k and v, then single-query attention
+ *     softmax(q K^T / sqrt(d_head)) V over the cached rows; section 4.1-4.3
+ *     for MQA, GQA and the latent (MLA) cache.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Every tensor pointer is a DEVICE pointer (hipMalloc'd or a torch
+ *    tensor's data_ptr) unless a parameter says "host". All tensors are dense,
+ *    row-major (last dimension fastest) and 16-byte aligned.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). Work
+ *    is enqueued asynchronously on it; the caller keeps every argument alive
+ *    until that work has run.
+ *  - Element type: every tensor that holds cache-typed values (k, v, q, out,
+ *    latent rows, MLA weights) has the cache's dtype. Nothing is converted
+ *    silently; there is no per-call dtype argument.
+ *  - Index arrays (`cache_index`, `valid_lens`) are int32 device arrays of
+ *    length B. They stay on the device so a decode step has fixed pointers
+ *    and launch shapes and can be captured in a HIP graph.
+ *  - Host-checkable misuse returns a status and enqueues NOTHING (the cache
+ *    is unchanged). Device-side out-of-range indices cannot be seen by the
+ *    host without a sync, so the kernels skip the offending sequence (append
+ *    writes nothing for it, attention writes zeros for it) and raise a sticky
+ *    per-cache flag that kvc_check() reports as KVC_ERR_DEVICE_RANGE.
+ *  - No call allocates or synchronises except kvc_alloc, kvc_free and
+ *    kvc_check (and every call when the environment variable KVC_SYNC_CHECK=1
+ *    is set, which makes each launch synchronous and checked).
+ */
+#ifndef KVC_H
+#define KVC_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVC_OK = 0,
+  KVC_ERR_INVALID_ARG = 1,   /* NULL pointer, bad layer, bad shape or field */
+  KVC_ERR_CAPACITY = 2,      /* host-visible rows outside [0, max_context) */
+  KVC_ERR_OOM = 3,           /* device allocation failed */
+  KVC_ERR_DEVICE = 4,        /* a HIP runtime call or launch failed */
+  KVC_ERR_UNSUPPORTED = 5,   /* valid request this build does not implement */
+  KVC_ERR_DEVICE_RANGE = 6   /* a device-side index was out of range (kvc_check) */
+} kvc_status;
+
+typedef enum { KVC_F32 = 0, KVC_BF16 = 1 } kvc_dtype;
+
+/* KVC_ATTN_GQA covers MHA (n_kv_heads == n_heads), GQA and MQA
+ * (n_kv_heads == 1) with one code path; KVC_ATTN_MLA is the latent cache. */
+typedef enum { KVC_ATTN_GQA = 0, KVC_ATTN_MLA = 1 } kvc_attn;
+
+/* Static shape of a cache. Fields not used by the attention kind must be 0.
+ *
+ *  GQA: n_heads % n_kv_heads == 0; head_dim in {32, 64, 128, 256};
+ *       latent_dim = rope_dim = 0.
+ *       Layout: [n_layers][2 (K, V)][batch][n_kv_heads][max_context][head_dim].
+ *  MLA: n_kv_heads = 1; latent_dim = 512, rope_dim = 64, head_dim = 128
+ *       (per-head width of q_nope and of the output), bf16 only.
+ *       Layout: [n_layers][batch][max_context][latent_dim + rope_dim], each
+ *       row = latent c (latent_dim) then the rotary key kR (rope_dim).
+ *  Group of query head h: kv head h / (n_heads / n_kv_heads) (contiguous). */
+typedef struct {
+  int32_t attn;         /* kvc_attn */
+  int32_t dtype;        /* kvc_dtype */
+  int32_t n_layers;     /* >= 1 */
+  int32_t batch;        /* B in [1, 2048] */
+  int32_t n_heads;      /* H, query heads >= 1 */
+  int32_t n_kv_heads;   /* H_kv */
+  int32_t head_dim;     /* d_h */
+  int32_t max_context;  /* S >= 1, rows per sequence */
+  int32_t latent_dim;   /* MLA d_c */
+  int32_t rope_dim;     /* MLA d_R */
+} kvc_desc;
+
+typedef struct kvc_cache kvc_cache; /* opaque */
+
+/* Physical bytes of the cache region for `desc` (pure host, no device work).
+ * "10.3 - KV cache implementation details", section 2 / 4.2:
+ *   GQA: 2 * n_layers * n_kv_heads * head_dim * max_context * batch * p;
+ * section 4.3 (with the rotary key stored in the same row):
+ *   MLA: n_layers * (latent_dim + rope_dim) * max_context * batch * p;
+ * p = 4 (fp32) or 2 (bf16). Returns KVC_ERR_INVALID_ARG for a bad desc. */
+kvc_status kvc_bytes(const kvc_desc* desc, uint64_t* physical);
+
+/* Allocate a cache once, at full capacity ("AR Static KV-Cache"). If
+ * `external` is NULL the library hipMallocs the region and zero-fills it;
+ * otherwise `external` must point to >= kvc_bytes() device bytes, 256-byte
+ * aligned, which the caller owns and keeps alive until kvc_free (the library
+ * neither clears nor frees it). The library also allocates a fixed
+ * workspace for split-context partials and a device error flag.
+ * Runs on the current HIP device; synchronous. On failure *out is NULL. */
+kvc_status kvc_alloc(const kvc_desc* desc, void* external, kvc_cache** out);
+
+/* Release the cache (and its region unless external). NULL is a no-op.
+ * Synchronises the device first. */
+kvc_status kvc_free(kvc_cache* cache);
+
+/* Device pointers of one layer: GQA *k = [B][H_kv][S][d_h] keys, *v values;
+ * MLA *k = [B][S][latent_dim + rope_dim] rows and *v = NULL. Host only. */
+kvc_status kvc_layer_ptrs(const kvc_cache* cache, int32_t layer, void** k, void** v);
+
+/* Logical bytes of the live prefixes given HOST valid lengths [B]:
+ * the byte formula with max_context * batch replaced by sum_b n_b
+ * ("KV Cache Optimization ...", "File map": totalBytes reports logical bytes,
+ * physicalBytes the capacity). Host only. */
+kvc_status kvc_logical_bytes(const kvc_cache* cache, const int32_t* host_valid_lens, uint64_t* out);
+
+/* Prefill fill / migration into the static buffer: copy rows
+ * [start, start + t) of every sequence and KV head of `layer`.
+ *  GQA: k, v = [B][H_kv][t][d_h].   MLA: k = rows [B][t][latent_dim + rope_dim],
+ *  v must be NULL.
+ * ("KV-Cache Mechanics", "AR Static KV-Cache": prefill fills the cache from
+ * cache_index 0; "KV Cache Optimization ...", "File map": migrateToPreAlloc.)
+ * Bit copy. start < 0, t < 1 or start + t > max_context -> KVC_ERR_CAPACITY. */
+kvc_status kvc_prefill_fill(kvc_cache* cache, int32_t layer, const void* k, const void* v,
+                            int32_t start, int32_t t, void* stream);
+
+/* In-place append of t_new new rows per sequence at a per-sequence position:
+ * rows [cache_index[b], cache_index[b] + t_new) of sequence b get
+ * k_new[b], v_new[b]; no other byte of the cache changes.
+ *  GQA: k_new, v_new = [B][H_kv][t_new][d_h].
+ *  MLA: k_new = rows [B][t_new][latent_dim + rope_dim], v_new must be NULL.
+ *  cache_index: device int32 [B].
+ * ("KV Cache Optimization ...", "#2 ... After": slice-assign at the valid
+ * length; "10.3 ...", section 5 step 2: append k_t, v_t before attention.)
+ * A sequence with cache_index[b] < 0 or cache_index[b] + t_new > max_context
+ * is skipped and raises the device-range flag. t_new < 1 -> INVALID_ARG. */
+kvc_status kvc_append(kvc_cache* cache, int32_t layer, const void* k_new, const void* v_new,
+                      const int32_t* cache_index, int32_t t_new, void* stream);
+
+/* Single-query decode attention of every query head over rows [0, n_b):
+ *   n_b = valid_lens ? valid_lens[b] : cache_index[b] + 1
+ * (append at cache_index, then attend it: the new token is included).
+ *  GQA: q = [B][H][d_h], out = [B][H][d_h];
+ *       out[b,h] = softmax(sm_scale * K[b,g,:n_b] q[b,h]) V[b,g,:n_b],
+ *       g = h / (H / H_kv)  ("10.3 ...", section 5 step 2 and section 4.2).
+ *  MLA: q = absorbed queries [B][H][latent_dim + rope_dim],
+ *       out = latent output [B][H][latent_dim];
+ *       out[b,h] = softmax(sm_scale * R[b,:n_b] q[b,h]) R[b,:n_b,:latent_dim],
+ *       R = the cached rows (latent then rotary key).
+ * Accumulation is fp32; out is rounded to the cache dtype (nearest-even).
+ * n_b == 0 gives out[b] = 0. n_b < 0 or n_b > max_context gives out[b] = 0
+ * and raises the device-range flag. At least one of valid_lens and
+ * cache_index must be non-NULL. sm_scale must be finite and > 0. */
+kvc_status kvc_decode_attn(kvc_cache* cache, int32_t layer, const void* q, void* out,
+                           const int32_t* valid_lens, const int32_t* cache_index,
+                           float sm_scale, void* stream);
+
+/* Full latent (MLA) decode step for an MLA cache ("10.3 ...", section 4.3;
+ * "KV-Cache Mechanics", MHA vs GQA vs MLA comparison, "absorb" overhead):
+ *   q~[b,h]  = [ W_UK[h]^T q_nope[b,h] ; q_rope[b,h] ]
+ *   o~[b,h]  = kvc_decode_attn(q~) over the latent rows
+ *   out[b,h] = W_UV[h]^T o~[b,h]
+ * which equals attention with per-head keys [W_UK[h] c_j ; kR_j] and values
+ * W_UV[h]^T c_j. Shapes (d_n = d_v = head_dim):
+ *   q_nope [B][H][d_n], q_rope [B][H][rope_dim], w_uk [H][d_n][latent_dim],
+ *   w_uv [H][latent_dim][d_v], out [B][H][d_v]; all bf16.
+ * Valid lengths, errors and rounding as kvc_decode_attn. */
+kvc_status kvc_mla_decode(kvc_cache* cache, int32_t layer, const void* q_nope, const void* q_rope,
+                          const void* w_uk, const void* w_uv, void* out,
+                          const int32_t* valid_lens, const int32_t* cache_index,
+                          float sm_scale, void* stream);
+
+/* Force the number of persistent workgroups attention launches (0 restores
+ * the default: as many as the device keeps resident at once). The rows of
+ * all sequences and kv heads are divided evenly among them, so this only
+ * changes how the context is partitioned and the rounding order of the
+ * result. n must be in [0, *max_n of kvc_get_workgroups]. Host only. */
+kvc_status kvc_set_workgroups(kvc_cache* cache, int32_t n);
+
+/* The forced workgroup count (0 = default) and, if max_n is not NULL, the
+ * largest accepted value. Host only. */
+kvc_status kvc_get_workgroups(const kvc_cache* cache, int32_t* n, int32_t* max_n);
+
+/* Synchronise `stream`, then report and clear the sticky device-range flag:
+ * KVC_ERR_DEVICE_RANGE if any kernel since the last check skipped a
+ * sequence, KVC_ERR_DEVICE if the stream reported an error, else KVC_OK. */
+kvc_status kvc_check(kvc_cache* cache, void* stream);
+
+/* Static string for a status code. */
+const char* kvc_strerror(kvc_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVC_H */

@@ -1,0 +1,324 @@
+// Host side of libkvc.so: descriptor validation, byte accounting, the one
+// static allocation, layer pointer math, split planning and launches on the
+// caller's stream. Every entry point is declared in include/kvc.h.
+//
+// Byte formulas: "10.3 - KV cache implementation details", section 2 (and
+// 4.2 for H_kv, 4.3 for the latent cache); "KV-Cache Mechanics", "Memory
+// Formula". Allocation once at full capacity: "KV-Cache Mechanics", "AR
+// Static KV-Cache"; "KV Cache Optimization: GQA Audit, In-Place Buffers,
+// Persistent Prompts", "#2 In-place KV cache updates".
+
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+
+#include "kvc_internal.h"
+
+namespace {
+
+bool env_sync_check() {
+  const char* s = getenv("KVC_SYNC_CHECK");
+  return s && s[0] == '1';
+}
+
+int elem_size(int dtype) { return dtype == KVC_F32 ? 4 : (dtype == KVC_BF16 ? 2 : 0); }
+
+bool valid_gqa_head_dim(int d) { return d == 32 || d == 64 || d == 128 || d == 256; }
+
+kvc_status validate_desc(const kvc_desc* d) {
+  if (!d) return KVC_ERR_INVALID_ARG;
+  if (elem_size(d->dtype) == 0) return KVC_ERR_INVALID_ARG;
+  if (d->n_layers < 1 || d->batch < 1 || d->n_heads < 1 || d->max_context < 1) return KVC_ERR_INVALID_ARG;
+  if (d->batch > KVC_MAX_BATCH) return KVC_ERR_UNSUPPORTED;
+  if (d->attn == KVC_ATTN_GQA) {
+    if (d->n_kv_heads < 1 || d->n_heads % d->n_kv_heads != 0) return KVC_ERR_INVALID_ARG;
+    if (d->latent_dim != 0 || d->rope_dim != 0) return KVC_ERR_INVALID_ARG;
+    if (!valid_gqa_head_dim(d->head_dim)) return KVC_ERR_UNSUPPORTED;
+    return KVC_OK;
+  }
+  if (d->attn == KVC_ATTN_MLA) {
+    if (d->n_kv_heads != 1) return KVC_ERR_INVALID_ARG;
+    if (d->latent_dim < 1 || d->rope_dim < 0 || d->head_dim < 1) return KVC_ERR_INVALID_ARG;
+    if (d->dtype != KVC_BF16 || d->latent_dim != 512 || d->rope_dim != 64 || d->head_dim != 128)
+      return KVC_ERR_UNSUPPORTED;
+    return KVC_OK;
+  }
+  return KVC_ERR_INVALID_ARG;
+}
+
+// Exact product with overflow check (all factors positive).
+bool mul_u64(uint64_t a, uint64_t b, uint64_t* out) {
+  if (a != 0 && b > UINT64_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+kvc_status bytes_of(const kvc_desc* d, uint64_t* out) {
+  uint64_t x = 1;
+  uint64_t p = (uint64_t)elem_size(d->dtype);
+  uint64_t factors[6];
+  int n = 0;
+  if (d->attn == KVC_ATTN_GQA) {
+    // 2 * L * H_kv * d_h * S * B * p
+    factors[n++] = 2;
+    factors[n++] = (uint64_t)d->n_layers;
+    factors[n++] = (uint64_t)d->n_kv_heads * (uint64_t)d->head_dim;
+    factors[n++] = (uint64_t)d->max_context;
+    factors[n++] = (uint64_t)d->batch;
+    factors[n++] = p;
+  } else {
+    // L * (d_c + d_R) * S * B * p
+    factors[n++] = (uint64_t)d->n_layers;
+    factors[n++] = (uint64_t)(d->latent_dim + d->rope_dim);
+    factors[n++] = (uint64_t)d->max_context;
+    factors[n++] = (uint64_t)d->batch;
+    factors[n++] = p;
+  }
+  for (int i = 0; i < n; ++i)
+    if (!mul_u64(x, factors[i], &x)) return KVC_ERR_INVALID_ARG;
+  *out = x;
+  return KVC_OK;
+}
+
+kvc_status after_launch(kvc_cache* c, hipError_t e, hipStream_t stream) {
+  if (e != hipSuccess) return KVC_ERR_DEVICE;
+  if (c->sync_check) {
+    if (hipStreamSynchronize(stream) != hipSuccess) return KVC_ERR_DEVICE;
+    int32_t flag = 0;
+    if (hipMemcpy(&flag, c->err_flag, sizeof(flag), hipMemcpyDeviceToHost) != hipSuccess)
+      return KVC_ERR_DEVICE;
+    if (flag) return KVC_ERR_DEVICE_RANGE;  // left set for kvc_check
+  }
+  return KVC_OK;
+}
+
+bool layer_ok(const kvc_cache* c, int32_t layer) { return layer >= 0 && layer < c->d.n_layers; }
+
+}  // namespace
+
+extern "C" {
+
+kvc_status kvc_bytes(const kvc_desc* desc, uint64_t* physical) {
+  if (!physical) return KVC_ERR_INVALID_ARG;
+  kvc_status s = validate_desc(desc);
+  if (s != KVC_OK) return s;
+  return bytes_of(desc, physical);
+}
+
+kvc_status kvc_alloc(const kvc_desc* desc, void* external, kvc_cache** out) {
+  if (!out) return KVC_ERR_INVALID_ARG;
+  *out = nullptr;
+  kvc_status s = validate_desc(desc);
+  if (s != KVC_OK) return s;
+  if (desc->attn == KVC_ATTN_MLA) return KVC_ERR_UNSUPPORTED;  // latent kernels not built yet
+  if (external && ((uintptr_t)external % 256) != 0) return KVC_ERR_INVALID_ARG;
+  uint64_t bytes = 0;
+  s = bytes_of(desc, &bytes);
+  if (s != KVC_OK) return s;
+
+  kvc_cache* c = new (std::nothrow) kvc_cache();
+  if (!c) return KVC_ERR_OOM;
+  memset(c, 0, sizeof(*c));
+  c->d = *desc;
+  c->elem = elem_size(desc->dtype);
+  c->bytes = bytes;
+  c->sync_check = env_sync_check();
+  if (hipGetDevice(&c->device) != hipSuccess) { delete c; return KVC_ERR_DEVICE; }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, c->device) != hipSuccess) { delete c; return KVC_ERR_DEVICE; }
+  c->num_cus = prop.multiProcessorCount;
+
+  if (desc->attn == KVC_ATTN_GQA) {
+    c->row_elems = desc->head_dim;
+    c->kv_bytes = (uint64_t)desc->batch * desc->n_kv_heads * desc->max_context * desc->head_dim * c->elem;
+    c->layer_bytes = 2 * c->kv_bytes;
+  } else {
+    c->row_elems = desc->latent_dim + desc->rope_dim;
+    c->kv_bytes = 0;
+    c->layer_bytes = (uint64_t)desc->batch * desc->max_context * c->row_elems * c->elem;
+  }
+  c->max_workgroups = c->num_cus * KVC_MAX_WG_PER_CU;
+  const int acc_width = desc->attn == KVC_ATTN_GQA ? desc->head_dim : desc->latent_dim;
+  // a slot per (workgroup, segment) intersection, at most 16 heads each
+  c->ws_entries = ((uint64_t)c->max_workgroups + (uint64_t)desc->batch * desc->n_heads) * 16;
+
+  bool ok = true;
+  if (external) {
+    c->base = (uint8_t*)external;
+    c->owns_base = false;
+  } else {
+    ok = hipMalloc((void**)&c->base, bytes) == hipSuccess;
+    c->owns_base = ok;
+    if (ok) ok = hipMemset(c->base, 0, bytes) == hipSuccess;
+  }
+  if (ok) ok = hipMalloc((void**)&c->ws_acc, c->ws_entries * acc_width * sizeof(float)) == hipSuccess;
+  if (ok) ok = hipMalloc((void**)&c->ws_ml, c->ws_entries * 2 * sizeof(float)) == hipSuccess;
+  const uint64_t cnt_bytes = (uint64_t)desc->batch * desc->n_heads * sizeof(int32_t);
+  if (ok) ok = hipMalloc((void**)&c->ws_cnt, cnt_bytes) == hipSuccess;
+  if (ok) ok = hipMemset(c->ws_cnt, 0, cnt_bytes) == hipSuccess;
+  if (ok) ok = hipMalloc((void**)&c->err_flag, 256) == hipSuccess;
+  if (ok) ok = hipMemset(c->err_flag, 0, 256) == hipSuccess;
+  if (ok && desc->attn == KVC_ATTN_MLA) {
+    const uint64_t bh = (uint64_t)desc->batch * desc->n_heads;
+    ok = hipMalloc((void**)&c->ws_qabs, bh * c->row_elems * sizeof(uint16_t)) == hipSuccess;
+    if (ok) ok = hipMalloc((void**)&c->ws_olat, bh * desc->latent_dim * sizeof(uint16_t)) == hipSuccess;
+  }
+  if (ok) ok = hipDeviceSynchronize() == hipSuccess;
+  if (!ok) {
+    (void)hipGetLastError();
+    kvc_free(c);
+    return KVC_ERR_OOM;
+  }
+  *out = c;
+  return KVC_OK;
+}
+
+kvc_status kvc_free(kvc_cache* c) {
+  if (!c) return KVC_OK;
+  hipError_t e = hipDeviceSynchronize();
+  if (c->owns_base && c->base) (void)hipFree(c->base);
+  if (c->ws_acc) (void)hipFree(c->ws_acc);
+  if (c->ws_ml) (void)hipFree(c->ws_ml);
+  if (c->ws_cnt) (void)hipFree(c->ws_cnt);
+  if (c->err_flag) (void)hipFree(c->err_flag);
+  if (c->ws_qabs) (void)hipFree(c->ws_qabs);
+  if (c->ws_olat) (void)hipFree(c->ws_olat);
+  delete c;
+  return e == hipSuccess ? KVC_OK : KVC_ERR_DEVICE;
+}
+
+kvc_status kvc_layer_ptrs(const kvc_cache* c, int32_t layer, void** k, void** v) {
+  if (!c || !k || !v || !layer_ok(c, layer)) return KVC_ERR_INVALID_ARG;
+  uint8_t* l = c->base + (uint64_t)layer * c->layer_bytes;
+  *k = l;
+  *v = c->d.attn == KVC_ATTN_GQA ? (void*)(l + c->kv_bytes) : nullptr;
+  return KVC_OK;
+}
+
+kvc_status kvc_logical_bytes(const kvc_cache* c, const int32_t* host_valid_lens, uint64_t* out) {
+  if (!c || !host_valid_lens || !out) return KVC_ERR_INVALID_ARG;
+  uint64_t total = 0;
+  for (int b = 0; b < c->d.batch; ++b) {
+    if (host_valid_lens[b] < 0 || host_valid_lens[b] > c->d.max_context) return KVC_ERR_CAPACITY;
+    total += (uint64_t)host_valid_lens[b];
+  }
+  const uint64_t per_row = c->d.attn == KVC_ATTN_GQA
+                               ? 2ull * c->d.n_kv_heads * c->d.head_dim * c->elem
+                               : (uint64_t)c->row_elems * c->elem;
+  *out = (uint64_t)c->d.n_layers * per_row * total;
+  return KVC_OK;
+}
+
+kvc_status kvc_prefill_fill(kvc_cache* c, int32_t layer, const void* k, const void* v, int32_t start,
+                            int32_t t, void* stream) {
+  if (!c || !k || !layer_ok(c, layer)) return KVC_ERR_INVALID_ARG;
+  const bool gqa = c->d.attn == KVC_ATTN_GQA;
+  if (gqa ? !v : v != nullptr) return KVC_ERR_INVALID_ARG;
+  if (t < 1) return KVC_ERR_INVALID_ARG;
+  if (start < 0 || (int64_t)start + t > c->d.max_context) return KVC_ERR_CAPACITY;
+  uint8_t* kl;
+  uint8_t* vl;
+  kvc_layer_ptrs(c, layer, (void**)&kl, (void**)&vl);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = kvc_launch_copy_rows(k, v, kl, vl, c->d.batch, gqa ? c->d.n_kv_heads : 1, t,
+                                      c->row_elems * c->elem, c->d.max_context, nullptr, start,
+                                      c->err_flag, s);
+  return after_launch(c, e, s);
+}
+
+kvc_status kvc_append(kvc_cache* c, int32_t layer, const void* k_new, const void* v_new,
+                      const int32_t* cache_index, int32_t t_new, void* stream) {
+  if (!c || !k_new || !cache_index || !layer_ok(c, layer)) return KVC_ERR_INVALID_ARG;
+  const bool gqa = c->d.attn == KVC_ATTN_GQA;
+  if (gqa ? !v_new : v_new != nullptr) return KVC_ERR_INVALID_ARG;
+  if (t_new < 1) return KVC_ERR_INVALID_ARG;
+  if (t_new > c->d.max_context) return KVC_ERR_CAPACITY;
+  uint8_t* kl;
+  uint8_t* vl;
+  kvc_layer_ptrs(c, layer, (void**)&kl, (void**)&vl);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = kvc_launch_copy_rows(k_new, v_new, kl, vl, c->d.batch, gqa ? c->d.n_kv_heads : 1,
+                                      t_new, c->row_elems * c->elem, c->d.max_context, cache_index, 0,
+                                      c->err_flag, s);
+  return after_launch(c, e, s);
+}
+
+kvc_status kvc_decode_attn(kvc_cache* c, int32_t layer, const void* q, void* out,
+                           const int32_t* valid_lens, const int32_t* cache_index, float sm_scale,
+                           void* stream) {
+  if (!c || !q || !out || !layer_ok(c, layer)) return KVC_ERR_INVALID_ARG;
+  if (!valid_lens && !cache_index) return KVC_ERR_INVALID_ARG;
+  if (!(sm_scale > 0.0f) || sm_scale > 3.0e38f) return KVC_ERR_INVALID_ARG;
+  void* kl;
+  void* vl;
+  kvc_layer_ptrs(c, layer, &kl, &vl);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (c->d.attn == KVC_ATTN_GQA)
+    e = kvc_launch_gqa_decode(c, kl, vl, q, out, valid_lens, cache_index, sm_scale, s);
+  else
+    e = kvc_launch_mla_attn(c, kl, q, out, valid_lens, cache_index, sm_scale, s);
+  return after_launch(c, e, s);
+}
+
+kvc_status kvc_mla_decode(kvc_cache* c, int32_t layer, const void* q_nope, const void* q_rope,
+                          const void* w_uk, const void* w_uv, void* out, const int32_t* valid_lens,
+                          const int32_t* cache_index, float sm_scale, void* stream) {
+  if (!c || !q_nope || !q_rope || !w_uk || !w_uv || !out || !layer_ok(c, layer))
+    return KVC_ERR_INVALID_ARG;
+  if (c->d.attn != KVC_ATTN_MLA) return KVC_ERR_INVALID_ARG;
+  if (!valid_lens && !cache_index) return KVC_ERR_INVALID_ARG;
+  if (!(sm_scale > 0.0f) || sm_scale > 3.0e38f) return KVC_ERR_INVALID_ARG;
+  void* kl;
+  void* vl;
+  kvc_layer_ptrs(c, layer, &kl, &vl);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = kvc_launch_mla_absorb(c, q_nope, q_rope, w_uk, c->ws_qabs, s);
+  if (e == hipSuccess)
+    e = kvc_launch_mla_attn(c, kl, c->ws_qabs, c->ws_olat, valid_lens, cache_index, sm_scale, s);
+  if (e == hipSuccess) e = kvc_launch_mla_uproj(c, c->ws_olat, w_uv, out, s);
+  return after_launch(c, e, s);
+}
+
+kvc_status kvc_set_workgroups(kvc_cache* c, int32_t n) {
+  if (!c || n < 0 || n > c->max_workgroups) return KVC_ERR_INVALID_ARG;
+  c->workgroups_forced = n;
+  return KVC_OK;
+}
+
+kvc_status kvc_get_workgroups(const kvc_cache* c, int32_t* n, int32_t* max_n) {
+  if (!c || !n) return KVC_ERR_INVALID_ARG;
+  *n = c->workgroups_forced;
+  if (max_n) *max_n = c->max_workgroups;
+  return KVC_OK;
+}
+
+kvc_status kvc_check(kvc_cache* c, void* stream) {
+  if (!c) return KVC_ERR_INVALID_ARG;
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return KVC_ERR_DEVICE;
+  int32_t flag = 0;
+  if (hipMemcpy(&flag, c->err_flag, sizeof(flag), hipMemcpyDeviceToHost) != hipSuccess)
+    return KVC_ERR_DEVICE;
+  if (flag) {
+    if (hipMemset(c->err_flag, 0, sizeof(int32_t)) != hipSuccess) return KVC_ERR_DEVICE;
+    if (hipDeviceSynchronize() != hipSuccess) return KVC_ERR_DEVICE;
+    return KVC_ERR_DEVICE_RANGE;
+  }
+  return KVC_OK;
+}
+
+const char* kvc_strerror(kvc_status s) {
+  switch (s) {
+    case KVC_OK: return "ok";
+    case KVC_ERR_INVALID_ARG: return "invalid argument";
+    case KVC_ERR_CAPACITY: return "rows outside the cache capacity";
+    case KVC_ERR_OOM: return "device allocation failed";
+    case KVC_ERR_DEVICE: return "HIP runtime error";
+    case KVC_ERR_UNSUPPORTED: return "unsupported configuration";
+    case KVC_ERR_DEVICE_RANGE: return "device-side index out of range (sequence skipped)";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,850 @@
+// Decode attention over the static cache (MHA / GQA / MQA).
+//
+// What is computed ("10.3 - KV cache implementation details", section 5
+// step 2, and section 4.1-4.2 for shared key/value heads): for every
+// sequence b and query head h, with kv head g = h / (H / H_kv) and
+// n = n_b valid rows,
+//     out[b,h] = softmax(sm_scale * K[b,g,0:n] q[b,h]) V[b,g,0:n].
+// Rows at or past n are never loaded ("KV Cache Optimization ...", "#2 ...
+// After": reads stop at the valid length).
+//
+// How (flash-decoding style, exact up to rounding order):
+//  - Work space. A "segment" is the valid rows [0, n_b) of one (sequence,
+//    kv head, head chunk); segments are laid end to end in one row space of
+//    R = sum_b n_b * H_kv * chunks rows. The grid is persistent: exactly as
+//    many 256-thread workgroups as the chip keeps resident, and workgroup w
+//    takes rows [w R / W, (w + 1) R / W) of that space (stream-K style), so
+//    every workgroup streams the same number of rows whatever the ragged
+//    valid lengths are, in one round. The part of a segment inside one
+//    workgroup (a "piece") is processed as a unit.
+//  - A piece is streamed ONCE and applied to all query heads of its head
+//    chunk. bf16 caches (MfmaPiece): each wave takes 16-row tiles in turn;
+//    q.k is one v_mfma_f32_16x16x32_bf16 per 32 dims with the 16 K rows as
+//    the A operand (loaded straight from HBM as 16-byte vectors) and the
+//    chunk's query heads, zero-padded to 16, as the B operand; the score
+//    tile that comes out is exactly the A operand of p.v
+//    (v_mfma_f32_16x16x16_bf16, K = the 16 rows), and V reaches its B
+//    operand through a row-major, skewed LDS tile read back with
+//    ds_read_b64_tr_b16 (one transpose read per 16 output columns). Each
+//    wave keeps its next tile in flight in registers while it uses the
+//    current one. fp32 caches (ValuPiece): one row per LPR consecutive
+//    lanes, FMA partial dots summed with DPP adds (quad_perm,
+//    row_half_mirror, row_mirror) and FMA accumulation. Softmax is the fp32
+//    online form in log2 units in both.
+//  - The waves (and, for fp32, a wave's row slots) are combined at the end
+//    of a piece (cross-lane shuffles, then LDS). A piece that is a whole
+//    segment is normalised and written directly. Otherwise it stores its
+//    partial (m, l, acc[D]) to slot w + s of the workspace (unique per
+//    workgroup w and segment s) with device-coherent stores, waits for them
+//    to complete and counts itself in on the segment's counter; the last
+//    piece to arrive merges all of them with exp2(m_p - m*) weights and
+//    resets the counter (no device-scope fence: see put/get below). One
+//    kernel per call.
+// Empty sequences (n = 0) give zeros; out-of-range n gives zeros and raises
+// the sticky device flag.
+
+#include <math.h>
+
+#include <type_traits>
+
+#include "kvc_internal.h"
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazy = 8.0f;  // log2 headroom before the running maximum is moved (VALU piece)
+constexpr float kLazyMfma = 64.0f;
+constexpr int kBufWord3 = 0x00020000;  // raw buffer resource word 3 (32-bit data format)  // the same for the matrix-core piece (fp32 sums, bf16 P)
+constexpr int kWaves = 4;      // waves per workgroup
+constexpr int kThreads = 64 * kWaves;
+
+template <typename T>
+struct Storage;
+template <>
+struct Storage<float> {  // fp32: 4 elements per 16-byte vector
+  static constexpr int kEPV = 4;
+};
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Cross-lane move within a row of 16 lanes. All patterns used here are
+// permutations, so every source lane is valid; bound_ctrl lets the compiler
+// fold the move into the consuming add (v_add_f32_dpp).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over aligned groups of LPR lanes; every lane of a group gets the sum.
+template <int LPR>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (LPR >= 2) x += dpp<0xB1>(x);    // quad_perm(1,0,3,2): lane ^ 1
+  if constexpr (LPR >= 4) x += dpp<0x4E>(x);    // quad_perm(2,3,0,1): lane ^ 2
+  if constexpr (LPR >= 8) x += dpp<0x141>(x);   // row_half_mirror: other quad of the 8
+  if constexpr (LPR >= 16) x += dpp<0x140>(x);  // row_mirror: other half of the 16
+  if constexpr (LPR >= 32) x += __shfl_xor(x, 16);
+  if constexpr (LPR >= 64) x += __shfl_xor(x, 32);
+  return x;
+}
+
+// Partial dot product of one 16-byte vector of q with one of k.
+__device__ __forceinline__ float vec_dot(const uint4& q, const uint4& k, uint16_t) {
+  float s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.x),
+                                            __builtin_bit_cast(bf16x2_t, k.x), 0.0f, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.y),
+                                      __builtin_bit_cast(bf16x2_t, k.y), s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.z),
+                                      __builtin_bit_cast(bf16x2_t, k.z), s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.w),
+                                      __builtin_bit_cast(bf16x2_t, k.w), s, false);
+  return s;
+}
+__device__ __forceinline__ float vec_dot(const uint4& q, const uint4& k, float) {
+  float s = __uint_as_float(q.x) * __uint_as_float(k.x);
+  s = fmaf(__uint_as_float(q.y), __uint_as_float(k.y), s);
+  s = fmaf(__uint_as_float(q.z), __uint_as_float(k.z), s);
+  s = fmaf(__uint_as_float(q.w), __uint_as_float(k.w), s);
+  return s;
+}
+
+// 16-byte vector -> fp32 elements.
+__device__ __forceinline__ void vec_unpack(const uint4& v, float (&f)[8], uint16_t) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+__device__ __forceinline__ void vec_unpack(const uint4& v, float (&f)[4], float) {
+  f[0] = __uint_as_float(v.x);
+  f[1] = __uint_as_float(v.y);
+  f[2] = __uint_as_float(v.z);
+  f[3] = __uint_as_float(v.w);
+}
+
+// fp32 -> bf16 bits, round to nearest, ties to even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x0040u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ void store_out(uint16_t* p, float f) { *p = bf16_rne(f); }
+__device__ __forceinline__ void store_out(float* p, float f) { *p = f; }
+
+// Valid rows of sequence b as the kernels use them: out-of-range lengths
+// count as 0 (the sequence is skipped and flagged).
+__device__ __forceinline__ int seq_rows(const int32_t* valid_lens, const int32_t* cache_index, int b,
+                                        int max_context, bool* bad) {
+  const int n = valid_lens ? valid_lens[b] : cache_index[b] + 1;
+  *bad = n < 0 || n > max_context;
+  return *bad ? 0 : n;
+}
+
+// Partials are exchanged between workgroups that may sit on different XCDs
+// (each with its own L2). They are written and read with device-scope
+// relaxed atomic accesses (global_store/load ... sc1), which are coherent at
+// device scope per location; a writer waits for its stores to complete
+// (vmcnt(0)) before it counts itself in, and the last arrival reads them
+// back. This avoids the full-L2 writeback/invalidate of a device-scope fence.
+__device__ __forceinline__ void put(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float get(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// s_waitcnt vmcnt(0) (expcnt, lgkmcnt left alone): this thread's stores are done
+__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+struct DecodeArgs {
+  const void* k;               // layer keys   [B][H_kv][S][D]
+  const void* v;               // layer values [B][H_kv][S][D]
+  const void* q;               // [B][H][D]
+  void* out;                   // [B][H][D]
+  const int32_t* valid_lens;   // [B] or null
+  const int32_t* cache_index;  // [B] or null
+  float scale_log2;
+  int batch, n_heads, n_kv_heads, max_context;
+  int head_chunks;             // chunks per kv head's query group
+  int chunk_heads;             // query heads per chunk (group / head_chunks)
+  int n_wg;                    // persistent grid size W
+  float* ws_acc;               // [slot][GC][D]
+  float* ws_ml;                // [slot][GC][2]
+  int32_t* ws_cnt;             // [B * H_kv * chunks] arrival counters (self-resetting)
+  int32_t* err_flag;
+};
+
+__device__ __forceinline__ long long wg_lo(int w, long long R, int W) { return (long long)w * R / W; }
+
+// Workgroup whose row range contains row x of the row space.
+__device__ __forceinline__ int wg_of(long long x, long long R, int W) {
+  int w = (int)(x * W / R);
+  while (w + 1 < W && wg_lo(w + 1, R, W) <= x) ++w;
+  while (w > 0 && wg_lo(w, R, W) > x) --w;
+  return w;
+}
+
+constexpr int kMaxPiecesPerSegment = 32;  // grid cap: at most ~32 workgroups per segment
+constexpr int kMinRowsPerWorkgroup = 64;  // and at least 64 rows each (no empty ranges)
+
+// Workgroups that share the row space: the launched grid, capped so every
+// workgroup gets >= kMinRowsPerWorkgroup rows and a segment is cut into at
+// most ~kMaxPiecesPerSegment pieces (bounds the merge of one segment).
+__device__ __forceinline__ int effective_wg(int n_wg, long long R, long long segments) {
+  long long w = n_wg;
+  w = min(w, max(1LL, segments * kMaxPiecesPerSegment));
+  w = min(w, max(1LL, R / kMinRowsPerWorkgroup));
+  return (int)w;
+}
+
+// A piece that is part of a segment (only a workgroup's first and last
+// piece can be) is recorded while the workgroup streams on; at the end the
+// workgroup waits once for all of its partial stores, counts its pieces in,
+// and for each segment where it arrived last merges all pieces:
+//   m* = max_p m_p, l* = sum_p l_p 2^(m_p - m*), out = sum_p acc_p 2^(m_p - m*) / l*,
+// writes the chunk's output rows and resets the counter.
+struct SplitPiece {
+  long long s, seg_start;
+  int n, b, h0;
+};
+
+template <typename T, int D, int SH>
+__device__ void finish_splits(const DecodeArgs& a, const SplitPiece* sp, int nsp, int* s_flag, long long R,
+                              int W) {
+  wait_stores();
+  __syncthreads();
+  if (threadIdx.x < nsp) {
+    const SplitPiece& q = sp[threadIdx.x];
+    const int w0 = wg_of(q.seg_start, R, W);
+    const int w1 = wg_of(q.seg_start + q.n - 1, R, W);
+    const int old = __hip_atomic_fetch_add(a.ws_cnt + q.s, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_flag[threadIdx.x * 3 + 0] = (old == w1 - w0) ? 1 : 0;
+    s_flag[threadIdx.x * 3 + 1] = w0;
+    s_flag[threadIdx.x * 3 + 2] = w1 - w0 + 1;
+  }
+  __syncthreads();
+  const int gc = a.chunk_heads;
+  constexpr int K = 8;  // pieces loaded together
+  for (int k = 0; k < nsp; ++k) {
+    if (!s_flag[k * 3]) continue;
+    const SplitPiece& q = sp[k];
+    const int w0 = s_flag[k * 3 + 1];
+    const int np = s_flag[k * 3 + 2];
+    for (int idx = threadIdx.x; idx < gc * D; idx += kThreads) {
+      const int h = idx / D;
+      const int d = idx - h * D;
+      auto entry = [&](int p) { return ((size_t)(w0 + p + q.s)) * SH + h; };
+      float mx = -INFINITY;
+      for (int p = 0; p < np; ++p) mx = fmaxf(mx, get(a.ws_ml + entry(p) * 2));
+      float x = 0.0f, lsum = 0.0f;
+      for (int p0 = 0; p0 < np; p0 += K) {
+        float mm[K], ll[K], aa[K];
+#pragma unroll
+        for (int i = 0; i < K; ++i) {
+          const int pc = min(p0 + i, np - 1);
+          mm[i] = get(a.ws_ml + entry(pc) * 2);
+          ll[i] = get(a.ws_ml + entry(pc) * 2 + 1);
+          aa[i] = get(a.ws_acc + entry(pc) * D + d);
+        }
+#pragma unroll
+        for (int i = 0; i < K; ++i) {
+          const float f = (p0 + i < np) ? __builtin_amdgcn_exp2f(mm[i] - mx) : 0.0f;
+          x = fmaf(aa[i], f, x);
+          lsum = fmaf(ll[i], f, lsum);
+        }
+      }
+      store_out(reinterpret_cast<T*>(a.out) + ((size_t)q.b * a.n_heads + q.h0 + h) * D + d, x / lsum);
+    }
+    if (threadIdx.x == 0) __hip_atomic_store(a.ws_cnt + q.s, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+template <typename T, int D, int GC>
+struct ValuPiece {
+  using Elem = T;
+  static constexpr int kD = D;
+  static constexpr int kSlotHeads = GC;  // partial entries per workspace slot
+  static constexpr int EPV = Storage<T>::kEPV;  // elements per 16-byte vector
+  static constexpr int LPR = D / EPV;           // lanes per cached row
+  static constexpr int RPI = 64 / LPR;          // rows per wave instruction (row slots)
+#ifndef KVC_TILE_U
+  static constexpr int U = (GC >= 8) ? 2 : 4;   // row vectors per K (and V) per tile and lane
+#else
+  static constexpr int U = KVC_TILE_U;
+#endif
+  static constexpr int TILE = RPI * U;          // rows per wave per tile
+  static_assert(LPR >= 1 && LPR <= 64 && 64 % LPR == 0, "row must map onto a wave");
+
+  struct Smem {
+    float acc[kWaves][GC][D];
+    float m[kWaves][GC];
+    float l[kWaves][GC];
+  };
+
+  // Rows [r_begin, r_end) of segment (b, g, chunk). Writes the normalised
+  // output when the piece is the whole segment, else the partial of `slot`.
+  static __device__ __forceinline__ void run(const DecodeArgs& a, Smem& sm, int b, int g, int chunk, int r_begin,
+                             int r_end, bool whole, long long slot) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int rs = lane / LPR;          // row slot of this lane
+    const int vec = lane - rs * LPR;    // which 16-byte vector of the row this lane owns
+    const int h0 = g * (a.n_heads / a.n_kv_heads) + chunk * GC;
+    const float scale_log2 = a.scale_log2;
+
+    uint4 qv[GC];
+#pragma unroll
+    for (int j = 0; j < GC; ++j)
+      qv[j] = reinterpret_cast<const uint4*>(reinterpret_cast<const T*>(a.q) +
+                                             ((size_t)b * a.n_heads + h0 + j) * D)[vec];
+
+    float m[GC], l[GC], acc[GC][EPV];
+#pragma unroll
+    for (int j = 0; j < GC; ++j) {
+      m[j] = -INFINITY;
+      l[j] = 0.0f;
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) acc[j][e] = 0.0f;
+    }
+
+    const size_t row0 = ((size_t)b * a.n_kv_heads + g) * (size_t)a.max_context;
+    const uint4* kp = reinterpret_cast<const uint4*>(a.k) + row0 * LPR + vec;
+    const uint4* vp = reinterpret_cast<const uint4*>(a.v) + row0 * LPR + vec;
+
+    // Tile loads never leave [r_begin, r_end): rows past the end are clamped
+    // to the last valid row (and masked in the softmax), so the next tile can
+    // be requested unconditionally while the current one is being used.
+    auto load_tile = [&](int base, uint4 (&kr)[U], uint4 (&vr)[U]) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int rc = min(base + u * RPI + rs, r_end - 1);
+        kr[u] = kp[(size_t)rc * LPR];
+        vr[u] = vp[(size_t)rc * LPR];
+      }
+    };
+    // One tile: raw scores q.k, then the online softmax in log2 units with
+    // the scale folded into one FMA (scale > 0, so max commutes with it).
+    // The running maximum is only moved (and acc, l rescaled) when some
+    // lane's tile maximum exceeds it by more than kLazy; otherwise the stale
+    // maximum is kept and p <= 2^kLazy. The final division by l makes the
+    // result the same for any reference maximum.
+    auto use_tile = [&](int base, const uint4 (&kr)[U], const uint4 (&vr)[U], auto full_tag) {
+      constexpr bool kFull = decltype(full_tag)::value;  // every row of the tile is live
+      float s[U][GC];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int j = 0; j < GC; ++j) s[u][j] = group_sum<LPR>(vec_dot(qv[j], kr[u], T()));
+      if constexpr (!kFull) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const bool live = base + u * RPI + rs < r_end;
+#pragma unroll
+          for (int j = 0; j < GC; ++j) s[u][j] = live ? s[u][j] : -INFINITY;
+        }
+      }
+      float nms[GC];  // -(reference maximum), finite
+#pragma unroll
+      for (int j = 0; j < GC; ++j) {
+        float tmax = s[0][j];
+#pragma unroll
+        for (int u = 1; u < U; ++u) tmax = fmaxf(tmax, s[u][j]);
+        const float cand = tmax * scale_log2;
+        if (__builtin_amdgcn_ballot_w64(cand > m[j] + kLazy)) {
+          const float mn = fmaxf(m[j], cand);
+          const float c = __builtin_amdgcn_exp2f(m[j] - ((mn == -INFINITY) ? 0.0f : mn));
+          l[j] *= c;
+#pragma unroll
+          for (int e = 0; e < EPV; ++e) acc[j][e] *= c;
+          m[j] = mn;
+        }
+        nms[j] = (m[j] == -INFINITY) ? 0.0f : -m[j];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float vf[EPV];
+        vec_unpack(vr[u], vf, T());
+#pragma unroll
+        for (int j = 0; j < GC; ++j) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[u][j], scale_log2, nms[j]));
+          l[j] += p;
+#pragma unroll
+          for (int e = 0; e < EPV; ++e) acc[j][e] = fmaf(p, vf[e], acc[j][e]);
+        }
+      }
+    };
+    using FullTile = std::integral_constant<bool, true>;
+    using EdgeTile = std::integral_constant<bool, false>;
+    auto use_any = [&](int base, const uint4 (&kr)[U], const uint4 (&vr)[U]) {
+      if (base + TILE <= r_end) use_tile(base, kr, vr, FullTile());
+      else use_tile(base, kr, vr, EdgeTile());
+    };
+
+    // Software pipeline over the wave's tiles: two register buffers, the next
+    // tile always in flight while the current one is consumed. Tiles go in
+    // pairs; a second tile entirely past r_end is all-masked (clamped loads
+    // that contribute p = 0).
+    const int stride = kWaves * TILE;
+    int base = r_begin + wave * TILE;
+    uint4 ka[U], va[U], kb[U], vb[U];
+    load_tile(base, ka, va);
+    for (; base < r_end; base += 2 * stride) {
+      load_tile(base + stride, kb, vb);
+      use_any(base, ka, va);
+      load_tile(base + 2 * stride, ka, va);
+      use_any(base + stride, kb, vb);
+    }
+
+    // Combine the wave's row slots (lanes with the same vector index).
+#pragma unroll
+    for (int j = 0; j < GC; ++j) {
+      float mw = m[j];
+#pragma unroll
+      for (int off = LPR; off < 64; off <<= 1) mw = fmaxf(mw, __shfl_xor(mw, off));
+      const float f = __builtin_amdgcn_exp2f(m[j] - ((mw == -INFINITY) ? 0.0f : mw));
+      float lw = l[j] * f;
+#pragma unroll
+      for (int off = LPR; off < 64; off <<= 1) lw += __shfl_xor(lw, off);
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) {
+        float x = acc[j][e] * f;
+#pragma unroll
+        for (int off = LPR; off < 64; off <<= 1) x += __shfl_xor(x, off);
+        acc[j][e] = x;
+      }
+      m[j] = mw;
+      l[j] = lw;
+    }
+    if (rs == 0) {
+#pragma unroll
+      for (int j = 0; j < GC; ++j)
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) sm.acc[wave][j][vec * EPV + e] = acc[j][e];
+      if (vec == 0) {
+#pragma unroll
+        for (int j = 0; j < GC; ++j) {
+          sm.m[wave][j] = m[j];
+          sm.l[wave][j] = l[j];
+        }
+      }
+    }
+    __syncthreads();
+
+    // Combine the waves (a wave with no live row has m = -inf, weight 0).
+    for (int idx = threadIdx.x; idx < GC * D; idx += kThreads) {
+      const int j = idx / D;
+      const int d = idx - j * D;
+      float mx = sm.m[0][j];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) mx = fmaxf(mx, sm.m[w][j]);
+      float x = 0.0f, lsum = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float f = __builtin_amdgcn_exp2f(sm.m[w][j] - mx);  // mx finite: piece non-empty
+        x = fmaf(sm.acc[w][j][d], f, x);
+        lsum = fmaf(sm.l[w][j], f, lsum);
+      }
+      if (whole) {
+        store_out(reinterpret_cast<T*>(a.out) + ((size_t)b * a.n_heads + h0 + j) * D + d, x / lsum);
+      } else {
+        const size_t e = (size_t)slot * GC + j;
+        put(a.ws_acc + e * D + d, x);
+        if (d == 0) {
+          put(a.ws_ml + e * 2, mx);
+          put(a.ws_ml + e * 2 + 1, lsum);
+        }
+      }
+    }
+    __syncthreads();  // the shared buffers are reused by the next piece
+  }
+};
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// bf16 piece on the matrix cores (see the file comment). Lane l of a wave is
+// (g, j) = (l / 16, l % 16). MFMA 16x16x32: A lane holds A[j][8g..8g+7],
+// B lane holds B[8g..8g+7][j], D lane holds D[4g..4g+3][j]; 16x16x16: the
+// same with 4g..4g+3 in place of 8g..8g+7.
+template <int D>
+struct MfmaPiece {
+  using Elem = uint16_t;
+  static constexpr int kD = D;
+  static constexpr int kSlotHeads = 16;        // partial entries per workspace slot
+  static constexpr int KS = D / 32;            // q.k steps of 32 dims
+  static constexpr int NB = D / 16;            // p.v output column blocks
+  static constexpr int TR = 16;                // rows per tile
+  static constexpr int CPR = D / 8;            // 16-byte chunks per row
+  static constexpr int VCH = TR * CPR / 64;    // V chunks per lane per tile
+  static constexpr int VSTRIDE = 2 * D + 32;   // bytes per staged V row (skew spreads LDS banks)
+#ifdef KVC_MFMA_NBUF
+  static constexpr int NBUF = KVC_MFMA_NBUF;
+#else
+  static constexpr int NBUF = D <= 64 ? 3 : 2; // register tiles in the ring (register budget)
+#endif
+  static_assert(D % 32 == 0 && VCH >= 1 && TR * CPR % 64 == 0, "head_dim must be 32..256");
+
+  struct Smem {
+    union {
+      unsigned char v[kWaves][TR * VSTRIDE];  // per-wave V staging (tile loop)
+      struct {
+        float acc[kWaves][16][D];
+        float m[kWaves][16];
+        float l[kWaves][16];
+      } c;                                     // per-wave results (end of piece)
+    } u;
+  };
+
+  static __device__ __forceinline__ void run(const DecodeArgs& a, Smem& sm, int b, int kvg, int chunk,
+                                             int r_begin, int r_end, bool whole, long long slot) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int g = lane >> 4;
+    const int j = lane & 15;
+    const int gc = a.chunk_heads;
+    const int h0 = kvg * (a.n_heads / a.n_kv_heads) + chunk * gc;
+    const float scale_log2 = a.scale_log2;
+
+    // q as the B operand: column j is head h0 + j, zero past the chunk
+    bf16x8_t qb[KS];
+    const bool real = j < gc;
+    const uint16_t* qh =
+        reinterpret_cast<const uint16_t*>(a.q) + ((size_t)b * a.n_heads + h0 + (real ? j : 0)) * D;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      u32x4_t v = *reinterpret_cast<const u32x4_t*>(qh + 32 * k + 8 * g);
+      v = real ? v : u32x4_t{0u, 0u, 0u, 0u};
+      qb[k] = __builtin_bit_cast(bf16x8_t, v);
+    }
+
+    f32x4_t o[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) o[nb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    float m = -INFINITY;  // reference maximum of head column j (log2 units)
+    float l = 0.0f;       // this lane's share of the softmax denominator of column j
+
+    const size_t row0 = ((size_t)b * a.n_kv_heads + kvg) * (size_t)a.max_context;
+    const uint16_t* kbase = reinterpret_cast<const uint16_t*>(a.k) + row0 * D;
+    const uint16_t* vbase = reinterpret_cast<const uint16_t*>(a.v) + row0 * D;
+    unsigned char* vs = sm.u.v[wave];
+
+    // Buffer resources spanning exactly the valid rows [0, r_end) of this
+    // (sequence, kv head): loads of rows past the end (the tail of the last
+    // tile, prefetches past the piece) return zeros without touching memory,
+    // and their scores are masked below.
+    const int nbytes = r_end * (2 * D);
+    const __amdgpu_buffer_rsrc_t kres = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, 0, nbytes, kBufWord3);
+    const __amdgpu_buffer_rsrc_t vres = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, 0, nbytes, kBufWord3);
+    const int koff = j * (2 * D) + 16 * g;  // K row base + j, dims 8g.. of each 32-dim step
+    const int voff = lane * 16;             // V tile as contiguous 16-byte chunks
+
+    auto load_tile = [&](int base, bf16x8_t (&kr)[KS], u32x4_t (&vr)[VCH]) {
+      const int kb = base * (2 * D) + koff;
+#pragma unroll
+      for (int k = 0; k < KS; ++k)
+        kr[k] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(kres, kb + 64 * k, 0, 0));
+      const int vb = base * (2 * D) + voff;
+#pragma unroll
+      for (int i = 0; i < VCH; ++i) vr[i] = __builtin_amdgcn_raw_buffer_load_b128(vres, vb + 1024 * i, 0, 0);
+    };
+    auto use_tile = [&](int base, const bf16x8_t (&kr)[KS], const u32x4_t (&vr)[VCH]) {
+      // stage V row-major in LDS
+#pragma unroll
+      for (int i = 0; i < VCH; ++i) {
+        const int f = i * 64 + lane;
+        *reinterpret_cast<u32x4_t*>(vs + (f / CPR) * VSTRIDE + (f % CPR) * 16) = vr[i];
+      }
+      // scores: s[t] = K[row base + 4g + t] . q[head column j]
+      f32x4_t s = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int k = 0; k < KS; ++k) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[k], qb[k], s, 0, 0, 0);
+      if (base + TR > r_end) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) s[t] = (base + 4 * g + t < r_end) ? s[t] : -INFINITY;
+      }
+      // online softmax with a lazily moved reference maximum: p and the bf16
+      // P operand keep full relative precision up to 2^kLazyMfma, so the
+      // reference is only moved (and o rescaled) when a score exceeds it by
+      // that much, which in practice happens only on a wave's first tile
+      const float cand = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])) * scale_log2;
+      if (__builtin_amdgcn_ballot_w64(cand > m + kLazyMfma)) {
+        float mt = fmaxf(cand, __shfl_xor(cand, 16));
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        const float mn = fmaxf(m, mt);
+        const float c = __builtin_amdgcn_exp2f(m - ((mn == -INFINITY) ? 0.0f : mn));
+        l *= c;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float ct = __shfl(c, 4 * g + t);  // factor of output row (head column) 4g + t
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) o[nb][t] *= ct;
+        }
+        m = mn;
+      }
+      const float nm = (m == -INFINITY) ? 0.0f : -m;
+      float p[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        p[t] = __builtin_amdgcn_exp2f(fmaf(s[t], scale_log2, nm));
+        l += p[t];
+      }
+      s16x4_t pa;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) pa[t] = __builtin_bit_cast(short, (__bf16)p[t]);
+      // p.v: B operand = V[base + 4g + t][16 nb + j] by one transpose read
+      const unsigned char* vrow = vs + (4 * g + (j >> 2)) * VSTRIDE + 8 * (j & 3);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const s16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4_t*)(vrow + 32 * nb));
+        o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, o[nb], 0, 0, 0);
+      }
+    };
+
+    // Software pipeline: a ring of NBUF register tiles, NBUF - 1 of them in
+    // flight while one is used. Loads are unconditional (rows past r_end read
+    // as zeros), and tiles past r_end are skipped, so every wave keeps its
+    // prefetch going.
+    const int stride = kWaves * TR;
+    int base = r_begin + wave * TR;
+    bf16x8_t kbuf[NBUF][KS];
+    u32x4_t vbuf[NBUF][VCH];
+#pragma unroll
+    for (int i = 0; i < NBUF - 1; ++i) load_tile(base + i * stride, kbuf[i], vbuf[i]);
+    for (; base < r_end; base += NBUF * stride) {
+#pragma unroll
+      for (int i = 0; i < NBUF; ++i) {
+        load_tile(base + (i + NBUF - 1) * stride, kbuf[(i + NBUF - 1) % NBUF], vbuf[(i + NBUF - 1) % NBUF]);
+        if (base + i * stride < r_end) use_tile(base + i * stride, kbuf[i], vbuf[i]);
+      }
+    }
+
+    // denominators: sum the lane shares of each head column
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    __syncthreads();  // every wave is done with its V staging area
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int i = 4 * g + t;
+      if (i < gc) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) sm.u.c.acc[wave][i][16 * nb + j] = o[nb][t];
+      }
+    }
+    if (g == 0 && j < gc) {
+      sm.u.c.m[wave][j] = m;
+      sm.u.c.l[wave][j] = l;
+    }
+    __syncthreads();
+
+    // Combine the waves (a wave with no live row has m = -inf, weight 0).
+    for (int idx = threadIdx.x; idx < gc * D; idx += kThreads) {
+      const int h = idx / D;
+      const int d = idx - h * D;
+      float mx = sm.u.c.m[0][h];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) mx = fmaxf(mx, sm.u.c.m[w][h]);
+      float x = 0.0f, lsum = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float f = __builtin_amdgcn_exp2f(sm.u.c.m[w][h] - mx);
+        x = fmaf(sm.u.c.acc[w][h][d], f, x);
+        lsum = fmaf(sm.u.c.l[w][h], f, lsum);
+      }
+      if (whole) {
+        store_out(reinterpret_cast<uint16_t*>(a.out) + ((size_t)b * a.n_heads + h0 + h) * D + d, x / lsum);
+      } else {
+        const size_t e = (size_t)slot * kSlotHeads + h;
+        put(a.ws_acc + e * D + d, x);
+        if (d == 0) {
+          put(a.ws_ml + e * 2, mx);
+          put(a.ws_ml + e * 2 + 1, lsum);
+        }
+      }
+    }
+    __syncthreads();  // shared memory is reused by the next piece
+  }
+};
+
+// Persistent decode kernel: grid = W workgroups of 256 threads.
+template <class P>
+__global__ __launch_bounds__(kThreads)
+#ifdef KVC_WAVES_PER_EU
+__attribute__((amdgpu_waves_per_eu(KVC_WAVES_PER_EU, KVC_WAVES_PER_EU)))
+#endif
+void gqa_decode_kernel(DecodeArgs a) {
+  __shared__ typename P::Smem sm;
+  __shared__ int32_t s_prefix[KVC_MAX_BATCH + 1];
+
+  // Prefix sums of the (sanitised) valid lengths, by the first wave: 64
+  // sequences per pass, an inclusive shuffle scan within the wave and a
+  // running offset between passes; one barrier publishes them.
+  const int B = a.batch;
+  const int t = threadIdx.x;
+  if (t < 64) {
+    int carry = 0;
+    for (int b0 = 0; b0 < B; b0 += 64) {
+      const int b = b0 + t;
+      int n = 0;
+      if (b < B) {
+        bool bad;
+        n = seq_rows(a.valid_lens, a.cache_index, b, a.max_context, &bad);
+        if (bad && blockIdx.x == 0) atomicOr(a.err_flag, 1);
+      }
+      int x = n;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off);
+        x += (t >= off) ? y : 0;
+      }
+      if (b < B) s_prefix[b + 1] = carry + x;
+      carry += __shfl(x, 63);
+    }
+    if (t == 0) s_prefix[0] = 0;
+  }
+  __syncthreads();
+
+  const int HC = a.n_kv_heads * a.head_chunks;  // segments per sequence
+  const long long R = (long long)s_prefix[B] * HC;
+  const int w = blockIdx.x;
+
+  // Empty (or out-of-range) sequences get zero outputs, spread over the grid.
+  for (int bz = w; bz < B; bz += a.n_wg) {
+    if (s_prefix[bz + 1] == s_prefix[bz]) {
+      using T = typename P::Elem;
+      T* o = reinterpret_cast<T*>(a.out) + (size_t)bz * a.n_heads * P::kD;
+      for (int i = t; i < a.n_heads * P::kD; i += kThreads) store_out(o + i, 0.0f);
+    }
+  }
+
+  const int W = effective_wg(a.n_wg, R, (long long)B * HC);
+  if (w >= W) return;
+  long long x = wg_lo(w, R, W);
+  const long long hi = wg_lo(w + 1, R, W);
+  if (x >= hi) return;
+  __shared__ int s_flag[6];
+  __shared__ SplitPiece split[2];  // a workgroup's first and last piece may be parts of segments
+  int nsplit = 0;
+
+  // first segment holding row x: sequence by binary search, then head chunk
+  int lo_b = 0, hi_b = B - 1;
+  while (lo_b < hi_b) {
+    const int mid = (lo_b + hi_b + 1) >> 1;
+    if ((long long)s_prefix[mid] * HC <= x) lo_b = mid; else hi_b = mid - 1;
+  }
+  int b = lo_b;
+  while ((long long)s_prefix[b + 1] * HC <= x) ++b;  // skip empty sequences
+  int n = s_prefix[b + 1] - s_prefix[b];
+  int hc = (int)((x - (long long)s_prefix[b] * HC) / n);
+
+  while (x < hi) {
+    const long long seg_start = (long long)s_prefix[b] * HC + (long long)hc * n;
+    const long long seg_end = seg_start + n;
+    const long long piece_end = seg_end < hi ? seg_end : hi;
+    const int r_begin = (int)(x - seg_start);
+    const int r_end = (int)(piece_end - seg_start);
+    const long long s = (long long)b * HC + hc;
+    const bool whole = r_begin == 0 && r_end == n;
+    const int kvg = hc / a.head_chunks;
+    const int chunk = hc % a.head_chunks;
+    P::run(a, sm, b, kvg, chunk, r_begin, r_end, whole, (long long)w + s);
+    if (!whole && nsplit < 2) {
+      if (threadIdx.x == 0) {  // read after the barriers in finish_splits
+        split[nsplit].s = s;
+        split[nsplit].seg_start = seg_start;
+        split[nsplit].n = n;
+        split[nsplit].b = b;
+        split[nsplit].h0 = kvg * (a.n_heads / a.n_kv_heads) + chunk * a.chunk_heads;
+      }
+      ++nsplit;
+    }
+    x = piece_end;
+    if (x >= hi) break;
+    if (++hc == HC) {  // next sequence with rows
+      hc = 0;
+      do { ++b; } while (s_prefix[b + 1] == s_prefix[b]);
+      n = s_prefix[b + 1] - s_prefix[b];
+    }
+  }
+  if (nsplit > 0)
+    finish_splits<typename P::Elem, P::kD, P::kSlotHeads>(a, split, nsplit, s_flag, R, W);
+}
+
+template <class P, typename T, int D>
+hipError_t launch_piece(const kvc_cache* c, DecodeArgs a, int chunk_heads, hipStream_t stream) {
+  static int resident = 0;  // workgroups per CU this kernel keeps resident
+  if (resident == 0) {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, gqa_decode_kernel<P>, kThreads, 0) != hipSuccess ||
+        nb < 1)
+      nb = 1;
+    resident = nb;
+  }
+  const int group = c->d.n_heads / c->d.n_kv_heads;
+  a.chunk_heads = chunk_heads;
+  a.head_chunks = group / chunk_heads;
+  a.n_wg = c->workgroups_forced > 0 ? c->workgroups_forced : resident * c->num_cus;
+  if (a.n_wg > c->max_workgroups) a.n_wg = c->max_workgroups;
+  gqa_decode_kernel<P><<<dim3(a.n_wg), dim3(kThreads), 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+// bf16: matrix-core piece; the group is cut into chunks of at most 16 heads.
+template <int D>
+hipError_t launch_bf16(const kvc_cache* c, const DecodeArgs& a, hipStream_t st) {
+  const int group = c->d.n_heads / c->d.n_kv_heads;
+  int gc = group <= 16 ? group : 16;
+  while (group % gc != 0) --gc;
+  return launch_piece<MfmaPiece<D>, uint16_t, D>(c, a, gc, st);
+}
+
+// fp32: VALU piece with GC heads per chunk.
+template <int D>
+hipError_t launch_f32(const kvc_cache* c, const DecodeArgs& a, hipStream_t st) {
+  const int group = c->d.n_heads / c->d.n_kv_heads;
+  if (group % 8 == 0) return launch_piece<ValuPiece<float, D, 8>, float, D>(c, a, 8, st);
+  if (group % 4 == 0) return launch_piece<ValuPiece<float, D, 4>, float, D>(c, a, 4, st);
+  if (group % 2 == 0) return launch_piece<ValuPiece<float, D, 2>, float, D>(c, a, 2, st);
+  return launch_piece<ValuPiece<float, D, 1>, float, D>(c, a, 1, st);
+}
+
+}  // namespace
+
+hipError_t kvc_launch_gqa_decode(const kvc_cache* c, const void* k_layer, const void* v_layer,
+                                 const void* q, void* out, const int32_t* valid_lens,
+                                 const int32_t* cache_index, float sm_scale, hipStream_t stream) {
+  if (c->d.batch > KVC_MAX_BATCH || (long long)c->d.batch * c->d.n_heads > 0x7fffffffLL)
+    return hipErrorInvalidValue;
+  DecodeArgs a;
+  a.k = k_layer;
+  a.v = v_layer;
+  a.q = q;
+  a.out = out;
+  a.valid_lens = valid_lens;
+  a.cache_index = cache_index;
+  a.scale_log2 = sm_scale * kLog2e;
+  a.batch = c->d.batch;
+  a.n_heads = c->d.n_heads;
+  a.n_kv_heads = c->d.n_kv_heads;
+  a.head_chunks = 1;
+  a.chunk_heads = 1;
+  a.max_context = c->d.max_context;
+  a.n_wg = 1;
+  a.ws_acc = c->ws_acc;
+  a.ws_ml = c->ws_ml;
+  a.ws_cnt = c->ws_cnt;
+  a.err_flag = c->err_flag;
+  const bool bf16 = c->d.dtype == KVC_BF16;
+  switch (c->d.head_dim) {
+    case 32: return bf16 ? launch_bf16<32>(c, a, stream) : launch_f32<32>(c, a, stream);
+    case 64: return bf16 ? launch_bf16<64>(c, a, stream) : launch_f32<64>(c, a, stream);
+    case 128: return bf16 ? launch_bf16<128>(c, a, stream) : launch_f32<128>(c, a, stream);
+    case 256: return bf16 ? launch_bf16<256>(c, a, stream) : launch_f32<256>(c, a, stream);
+  }
+  return hipErrorInvalidValue;
+}

@@ -1,0 +1,68 @@
+// Internal declarations shared by the host library and the kernels of
+// libkvc.so. Nothing here is part of the C ABI (include/kvc.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvc.h"
+
+// Largest batch the attention kernels accept (their prefix sums of the
+// valid lengths live in LDS).
+#define KVC_MAX_BATCH 2048
+// Most persistent workgroups per CU the workspace is sized for.
+#define KVC_MAX_WG_PER_CU 8
+
+struct kvc_cache {
+  kvc_desc d;
+  int device;
+  int num_cus;
+  uint8_t* base;          // cache region (one allocation, lives until kvc_free)
+  bool owns_base;
+  uint64_t bytes;         // physical bytes of the region
+  int elem;               // bytes per element (4 fp32, 2 bf16)
+  uint64_t layer_bytes;   // bytes per layer (K and V together for GQA)
+  uint64_t kv_bytes;      // offset of V from K inside a layer (GQA)
+  int row_elems;          // elements per cached row: head_dim (GQA) or d_c + d_R (MLA)
+
+  // fixed workspace (allocated once by kvc_alloc)
+  int max_workgroups;     // num_cus * KVC_MAX_WG_PER_CU
+  uint64_t ws_entries;    // partial entries: (max_workgroups + batch * n_heads) * 16
+  float* ws_acc;          // [entry][acc_width] unnormalised partial outputs
+  float* ws_ml;           // [entry][2]  (reference maximum in log2 units, sum)
+  int32_t* ws_cnt;        // [batch * n_heads] per-segment arrival counters (zeroed once, self-resetting)
+  uint16_t* ws_qabs;      // MLA: absorbed queries [B][H][d_c + d_R] (bf16)
+  uint16_t* ws_olat;      // MLA: latent outputs   [B][H][d_c] (bf16)
+  int32_t* err_flag;      // sticky device-range flag
+  int32_t workgroups_forced;  // 0 = as many as the chip keeps resident
+  bool sync_check;        // KVC_SYNC_CHECK=1
+};
+
+// ---- launchers (defined in the kernel translation units) -------------------
+
+// Row copy into the cache: for each (b, g) of B*H_kv row groups, rows
+// [start_b, start_b + t) get src[b][g][0..t). start_b = dev_start ?
+// dev_start[b] : host_start. Sequences out of range are skipped and raise
+// *err_flag. row_bytes must be a multiple of 16.
+hipError_t kvc_launch_copy_rows(const void* src_k, const void* src_v, uint8_t* dst_k, uint8_t* dst_v,
+                                int batch, int n_kv_heads, int t, int row_bytes, int max_context,
+                                const int32_t* dev_start, int host_start, int32_t* err_flag,
+                                hipStream_t stream);
+
+// Persistent split-context GQA decode (pieces merged in the same kernel).
+hipError_t kvc_launch_gqa_decode(const kvc_cache* c, const void* k_layer, const void* v_layer,
+                                 const void* q, void* out, const int32_t* valid_lens,
+                                 const int32_t* cache_index, float sm_scale, hipStream_t stream);
+
+// Latent (MLA) decode over absorbed queries q_abs [B][H][d_c + d_R] (bf16)
+// into out_lat [B][H][d_c] (bf16).
+hipError_t kvc_launch_mla_attn(const kvc_cache* c, const void* rows_layer, const void* q_abs,
+                               void* out_lat, const int32_t* valid_lens, const int32_t* cache_index,
+                               float sm_scale, hipStream_t stream);
+
+// MLA query absorption q~ = [W_UK^T q_nope ; q_rope] and output up-projection
+// out = W_UV^T o~ (bf16 in/out, fp32 accumulation).
+hipError_t kvc_launch_mla_absorb(const kvc_cache* c, const void* q_nope, const void* q_rope,
+                                 const void* w_uk, uint16_t* q_abs, hipStream_t stream);
+hipError_t kvc_launch_mla_uproj(const kvc_cache* c, const uint16_t* o_lat, const void* w_uv,
+                                void* out, hipStream_t stream);

@@ -1,0 +1,318 @@
+"""Thin ctypes binding over libkvc.so (the C ABI declared in include/kvc.h).
+
+Argument marshalling only: every step of the decode path runs in the HIP
+kernels of the library. torch is used for device memory (tensors are passed
+by ``data_ptr()``) and for the current stream handle. The binding checks
+tensor shapes, dtypes, devices and contiguity before any call so that a
+kernel never sees a buffer smaller than its launch assumes.
+
+If the library has not been built, every call raises ``RuntimeError``:
+there is no fallback path.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkvc.so")
+
+KVC_OK, KVC_ERR_INVALID_ARG, KVC_ERR_CAPACITY, KVC_ERR_OOM = 0, 1, 2, 3
+KVC_ERR_DEVICE, KVC_ERR_UNSUPPORTED, KVC_ERR_DEVICE_RANGE = 4, 5, 6
+KVC_F32, KVC_BF16 = 0, 1
+KVC_ATTN_GQA, KVC_ATTN_MLA = 0, 1
+
+_DTYPES = {"f32": KVC_F32, "bf16": KVC_BF16}
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int32) for name in (
+        "attn", "dtype", "n_layers", "batch", "n_heads", "n_kv_heads", "head_dim",
+        "max_context", "latent_dim", "rope_dim")]
+
+    def __repr__(self):
+        return "Desc(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
+
+
+class KvcError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        msg = _lib.kvc_strerror(status).decode() if _lib is not None else str(status)
+        super().__init__(f"{where}: {msg} (status {status})")
+
+
+_p = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_SIGS = {
+    "kvc_bytes": [ctypes.POINTER(Desc), ctypes.POINTER(ctypes.c_uint64)],
+    "kvc_alloc": [ctypes.POINTER(Desc), _p, ctypes.POINTER(_p)],
+    "kvc_free": [_p],
+    "kvc_layer_ptrs": [_p, _i32, ctypes.POINTER(_p), ctypes.POINTER(_p)],
+    "kvc_logical_bytes": [_p, _p, ctypes.POINTER(ctypes.c_uint64)],
+    "kvc_prefill_fill": [_p, _i32, _p, _p, _i32, _i32, _p],
+    "kvc_append": [_p, _i32, _p, _p, _p, _i32, _p],
+    "kvc_decode_attn": [_p, _i32, _p, _p, _p, _p, ctypes.c_float, _p],
+    "kvc_mla_decode": [_p, _i32, _p, _p, _p, _p, _p, _p, _p, ctypes.c_float, _p],
+    "kvc_set_workgroups": [_p, _i32],
+    "kvc_get_workgroups": [_p, ctypes.POINTER(_i32), ctypes.POINTER(_i32)],
+    "kvc_check": [_p, _p],
+    "kvc_strerror": [ctypes.c_int],
+}
+
+_lib = None
+
+
+def load(path=LIB_PATH):
+    """Open libkvc.so and bind every entry point (raises if not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run __graft_entry__.build() first")
+    # torch ships its own HIP runtime with the same soname; importing it first
+    # makes libkvc.so bind to that one, so the process has a single runtime and
+    # torch's streams and allocations are valid handles for the library.
+    _torch()
+    lib = ctypes.CDLL(path)
+    lib.hipMemcpyAsync.argtypes = [_p, _p, ctypes.c_size_t, ctypes.c_int, _p]
+    lib.hipMemcpyAsync.restype = ctypes.c_int
+    for name, args in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_char_p if name == "kvc_strerror" else ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _call(name, *args):
+    st = getattr(load(), name)(*args)
+    if st != KVC_OK:
+        raise KvcError(st, name)
+
+
+def gqa_desc(n_layers, batch, n_heads, n_kv_heads, head_dim, max_context, dtype):
+    return Desc(KVC_ATTN_GQA, _DTYPES[dtype], n_layers, batch, n_heads, n_kv_heads, head_dim,
+                max_context, 0, 0)
+
+
+def mla_desc(n_layers, batch, n_heads, max_context, latent_dim=512, rope_dim=64, head_dim=128,
+             dtype="bf16"):
+    return Desc(KVC_ATTN_MLA, _DTYPES[dtype], n_layers, batch, n_heads, 1, head_dim, max_context,
+                latent_dim, rope_dim)
+
+
+def cache_bytes(desc):
+    out = ctypes.c_uint64(0)
+    _call("kvc_bytes", ctypes.byref(desc), ctypes.byref(out))
+    return out.value
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def torch_dtype(dtype):
+    torch = _torch()
+    return {"f32": torch.float32, "bf16": torch.bfloat16}[dtype]
+
+
+def to_device(a, device):
+    """numpy (uint16 bf16 bits / float32 / int32) -> contiguous torch tensor on device."""
+    torch = _torch()
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
+    elif a.dtype in (np.float32, np.int32):
+        t = torch.from_numpy(a)
+    else:
+        raise TypeError(f"unsupported array dtype {a.dtype}")
+    return t.to(device)
+
+
+def _stream(device):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+class Cache:
+    """One static cache (all layers) allocated once on the current device."""
+
+    def __init__(self, desc, external=None):
+        torch = _torch()
+        self.desc = desc
+        self.dtype = {KVC_F32: "f32", KVC_BF16: "bf16"}[desc.dtype]
+        self.device = torch.device("cuda", torch.cuda.current_device())
+        self.nbytes = cache_bytes(desc)
+        self._external = external
+        ext = None
+        if external is not None:
+            if not (external.is_cuda and external.is_contiguous()
+                    and external.numel() * external.element_size() >= self.nbytes):
+                raise ValueError("external buffer must be a contiguous device tensor of >= kvc_bytes")
+            ext = ctypes.c_void_p(external.data_ptr())
+        h = ctypes.c_void_p()
+        _call("kvc_alloc", ctypes.byref(desc), ext, ctypes.byref(h))
+        self._h = h
+
+    # -- shape helpers -------------------------------------------------------
+    @property
+    def is_mla(self):
+        return self.desc.attn == KVC_ATTN_MLA
+
+    @property
+    def row_width(self):
+        d = self.desc
+        return d.latent_dim + d.rope_dim if self.is_mla else d.head_dim
+
+    def _check(self, t, shape, dtype=None, name="tensor"):
+        torch = _torch()
+        want = torch_dtype(self.dtype) if dtype is None else dtype
+        if t.device != self.device:
+            raise ValueError(f"{name} must be on {self.device}, got {t.device}")
+        if t.dtype != want:
+            raise ValueError(f"{name} must be {want}, got {t.dtype}")
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+        if not t.is_contiguous() or t.data_ptr() % 16 != 0:
+            raise ValueError(f"{name} must be contiguous and 16-byte aligned")
+        return ctypes.c_void_p(t.data_ptr())
+
+    def _idx(self, t, name):
+        if t is None:
+            return None
+        return self._check(t, (self.desc.batch,), _torch().int32, name)
+
+    @property
+    def handle(self):
+        if self._h is None:
+            raise RuntimeError("cache already freed")
+        return self._h
+
+    # -- C ABI calls ---------------------------------------------------------
+    def layer_ptrs(self, layer):
+        k, v = ctypes.c_void_p(), ctypes.c_void_p()
+        _call("kvc_layer_ptrs", self.handle, layer, ctypes.byref(k), ctypes.byref(v))
+        return k.value, v.value
+
+    def layer_tensors(self, layer):
+        """Copies of one layer's region as torch tensors (K, V) or (rows, None)."""
+        torch = _torch()
+        d = self.desc
+        k_ptr, v_ptr = self.layer_ptrs(layer)
+        shape = (d.batch, d.max_context, self.row_width) if self.is_mla else \
+            (d.batch, d.n_kv_heads, d.max_context, d.head_dim)
+        n = int(np.prod(shape))
+        out = []
+        for ptr in (k_ptr, v_ptr):
+            if ptr is None:
+                out.append(None)
+                continue
+            t = torch.empty(shape, dtype=torch_dtype(self.dtype), device=self.device)
+            _memcpy_d2d(t.data_ptr(), ptr, n * t.element_size(), self.device)
+            out.append(t)
+        return tuple(out)
+
+    def logical_bytes(self, valid_lens):
+        v = np.ascontiguousarray(valid_lens, dtype=np.int32)
+        if v.shape != (self.desc.batch,):
+            raise ValueError("valid_lens must have shape [B]")
+        out = ctypes.c_uint64(0)
+        _call("kvc_logical_bytes", self.handle, v.ctypes.data_as(ctypes.c_void_p), ctypes.byref(out))
+        return out.value
+
+    def prefill_fill(self, layer, k, v, start):
+        d = self.desc
+        if self.is_mla:
+            t = k.shape[1]
+            kp = self._check(k, (d.batch, t, self.row_width), name="rows")
+            if v is not None:
+                raise ValueError("latent cache takes no v")
+            vp = None
+        else:
+            t = k.shape[2]
+            shape = (d.batch, d.n_kv_heads, t, d.head_dim)
+            kp, vp = self._check(k, shape, name="k"), self._check(v, shape, name="v")
+        _call("kvc_prefill_fill", self.handle, layer, kp, vp, start, t, _stream(self.device))
+
+    def append(self, layer, k_new, v_new, cache_index):
+        d = self.desc
+        if self.is_mla:
+            t = k_new.shape[1]
+            kp = self._check(k_new, (d.batch, t, self.row_width), name="rows_new")
+            if v_new is not None:
+                raise ValueError("latent cache takes no v_new")
+            vp = None
+        else:
+            t = k_new.shape[2]
+            shape = (d.batch, d.n_kv_heads, t, d.head_dim)
+            kp, vp = self._check(k_new, shape, name="k_new"), self._check(v_new, shape, name="v_new")
+        ci = self._idx(cache_index, "cache_index")
+        _call("kvc_append", self.handle, layer, kp, vp, ci, t, _stream(self.device))
+
+    def decode_attn(self, layer, q, out, valid_lens=None, cache_index=None, sm_scale=None):
+        d = self.desc
+        if self.is_mla:
+            qp = self._check(q, (d.batch, d.n_heads, self.row_width), name="q")
+            op = self._check(out, (d.batch, d.n_heads, d.latent_dim), name="out")
+        else:
+            qp = self._check(q, (d.batch, d.n_heads, d.head_dim), name="q")
+            op = self._check(out, (d.batch, d.n_heads, d.head_dim), name="out")
+        if sm_scale is None:
+            raise ValueError("sm_scale is required")
+        _call("kvc_decode_attn", self.handle, layer, qp, op, self._idx(valid_lens, "valid_lens"),
+              self._idx(cache_index, "cache_index"), float(sm_scale), _stream(self.device))
+
+    def mla_decode(self, layer, q_nope, q_rope, w_uk, w_uv, out, valid_lens=None, cache_index=None,
+                   sm_scale=None):
+        d = self.desc
+        B, H, dn, dc, dr = d.batch, d.n_heads, d.head_dim, d.latent_dim, d.rope_dim
+        args = [self._check(q_nope, (B, H, dn), name="q_nope"),
+                self._check(q_rope, (B, H, dr), name="q_rope"),
+                self._check(w_uk, (H, dn, dc), name="w_uk"),
+                self._check(w_uv, (H, dc, dn), name="w_uv"),
+                self._check(out, (B, H, dn), name="out")]
+        if sm_scale is None:
+            raise ValueError("sm_scale is required")
+        _call("kvc_mla_decode", self.handle, layer, *args, self._idx(valid_lens, "valid_lens"),
+              self._idx(cache_index, "cache_index"), float(sm_scale), _stream(self.device))
+
+    def set_workgroups(self, n):
+        """Force the persistent attention grid size (0 = device default)."""
+        _call("kvc_set_workgroups", self.handle, n)
+
+    def workgroups(self):
+        """(forced count or 0, largest accepted count)."""
+        n, mx = ctypes.c_int32(0), ctypes.c_int32(0)
+        _call("kvc_get_workgroups", self.handle, ctypes.byref(n), ctypes.byref(mx))
+        return n.value, mx.value
+
+    def check(self):
+        """Synchronise the current stream; raise KvcError on a device-range or HIP error."""
+        _call("kvc_check", self.handle, _stream(self.device))
+
+    def check_status(self):
+        """Like check() but return the status code instead of raising."""
+        return load().kvc_check(self.handle, _stream(self.device))
+
+    def free(self):
+        if self._h is not None:
+            _call("kvc_free", self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+def _memcpy_d2d(dst, src, nbytes, device):
+    """Device-to-device byte copy on the current stream, through the HIP
+    runtime that libkvc.so itself is bound to; waits for completion."""
+    st = load().hipMemcpyAsync(ctypes.c_void_p(dst), ctypes.c_void_p(src), ctypes.c_size_t(nbytes),
+                               ctypes.c_int(3), _stream(device))
+    if st != 0:
+        raise RuntimeError(f"hipMemcpyAsync failed ({st})")
+    _torch().cuda.current_stream(device).synchronize()

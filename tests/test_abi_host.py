@@ -1,0 +1,99 @@
+"""The C-ABI library on the host (no GPU needed): it loads, exports every
+entry point include/kvc.h declares, and its pure-host byte accounting
+matches the oracle. No call here touches the device."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from oracle import cache_bytes as cb
+from static_kv_cache_amd import kvc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvc.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvc_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kvc.LIB_PATH):
+        pytest.fail("libkvc.so is not built (run __graft_entry__.build())")
+    return kvc.load()
+
+
+def test_header_declares_expected_entry_points():
+    names = declared_functions()
+    for required in ("kvc_alloc", "kvc_prefill_fill", "kvc_append", "kvc_decode_attn",
+                     "kvc_mla_decode", "kvc_bytes", "kvc_free", "kvc_check"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(kvc.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(raw, n)]
+    assert not missing, f"not exported: {missing}"
+    assert set(declared_functions()) == set(kvc._SIGS), "binding and header disagree"
+
+
+@pytest.mark.parametrize("shape", [
+    (1, 1, 4, 4, 32, 128, "f32"),        # tiny MHA
+    (12, 8, 8, 8, 32, 512, "bf16"),      # DantinoX MHA
+    (12, 8, 8, 2, 32, 512, "bf16"),      # DantinoX GQA
+    (32, 16, 32, 8, 128, 4096, "bf16"),  # Llama-3-8B-shaped
+    (80, 1, 64, 8, 128, 32768, "bf16"),  # long context (80 layers)
+    (80, 1, 64, 64, 128, 4096, "bf16"),  # the Llama-2-70B printed example
+    (32, 1, 32, 32, 128, 1024, "f32"),   # the Llama-3 fp32 printed example
+])
+def test_kvc_bytes_matches_oracle(lib, shape):
+    L, B, H, Hkv, D, S, dt = shape
+    got = kvc.cache_bytes(kvc.gqa_desc(L, B, H, Hkv, D, S, dt))
+    assert got == cb.kv_cache_bytes(L, Hkv, D, S, B, 4 if dt == "f32" else 2)
+
+
+def test_kvc_bytes_printed_examples(lib):
+    assert kvc.cache_bytes(kvc.gqa_desc(80, 1, 64, 64, 128, 4096, "bf16")) == 10737418240
+    assert kvc.cache_bytes(kvc.gqa_desc(32, 1, 32, 32, 128, 1024, "f32")) == 1073741824
+    assert kvc.cache_bytes(kvc.gqa_desc(80, 1, 64, 8, 128, 32768, "bf16")) == 10737418240
+
+
+def test_kvc_bytes_latent(lib):
+    got = kvc.cache_bytes(kvc.mla_desc(1, 32, 16, 4096))
+    assert got == cb.mla_cache_bytes(1, 512, 4096, 32, 2, rope_dim=64) == 150994944
+
+
+@pytest.mark.parametrize("bad", [
+    dict(n_heads=6, n_kv_heads=4),      # H not a multiple of H_kv
+    dict(n_layers=0), dict(batch=0), dict(max_context=0), dict(n_kv_heads=0),
+    dict(dtype=7), dict(attn=3), dict(latent_dim=8), dict(batch=-4),
+])
+def test_kvc_bytes_rejects_bad_descriptors(lib, bad):
+    fields = dict(attn=0, dtype=1, n_layers=2, batch=2, n_heads=8, n_kv_heads=2, head_dim=32,
+                  max_context=64, latent_dim=0, rope_dim=0)
+    fields.update(bad)
+    d = kvc.Desc(**fields)
+    out = ctypes.c_uint64(0)
+    assert lib.kvc_bytes(ctypes.byref(d), ctypes.byref(out)) == kvc.KVC_ERR_INVALID_ARG
+
+
+def test_unsupported_head_dim_and_null(lib):
+    d = kvc.gqa_desc(1, 1, 4, 4, 48, 16, "bf16")
+    out = ctypes.c_uint64(0)
+    assert lib.kvc_bytes(ctypes.byref(d), ctypes.byref(out)) == kvc.KVC_ERR_UNSUPPORTED
+    assert lib.kvc_bytes(None, ctypes.byref(out)) == kvc.KVC_ERR_INVALID_ARG
+    assert lib.kvc_bytes(ctypes.byref(kvc.gqa_desc(1, 1, 4, 4, 32, 16, "bf16")), None) == kvc.KVC_ERR_INVALID_ARG
+
+
+def test_host_only_calls_reject_null_handles(lib):
+    k, v = ctypes.c_void_p(), ctypes.c_void_p()
+    assert lib.kvc_layer_ptrs(None, 0, ctypes.byref(k), ctypes.byref(v)) == kvc.KVC_ERR_INVALID_ARG
+    assert lib.kvc_set_workgroups(None, 64) == kvc.KVC_ERR_INVALID_ARG
+    assert lib.kvc_free(None) == kvc.KVC_OK
+    for s in range(7):
+        assert lib.kvc_strerror(s)
