@@ -83,7 +83,9 @@ typedef struct {
   int32_t n_heads;      /* H, query heads >= 1 */
   int32_t n_kv_heads;   /* H_kv */
   int32_t head_dim;     /* d_h */
-  int32_t max_context;  /* S >= 1, rows per sequence */
+  int32_t max_context;  /* S >= 1, rows per sequence; KVC_ERR_UNSUPPORTED when
+                           batch * (S + 1024) >= 2^31 or one (sequence, kv
+                           head) block S * head_dim * p >= 2^31 bytes */
   int32_t latent_dim;   /* MLA d_c */
   int32_t rope_dim;     /* MLA d_R */
 } kvc_desc;

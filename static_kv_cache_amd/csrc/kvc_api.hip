@@ -31,10 +31,16 @@ kvc_status validate_desc(const kvc_desc* d) {
   if (elem_size(d->dtype) == 0) return KVC_ERR_INVALID_ARG;
   if (d->n_layers < 1 || d->batch < 1 || d->n_heads < 1 || d->max_context < 1) return KVC_ERR_INVALID_ARG;
   if (d->batch > KVC_MAX_BATCH) return KVC_ERR_UNSUPPORTED;
+  // the decode row space (rows of all sequences plus per-segment start-up
+  // rows) and byte offsets within one sequence's rows are 32-bit
+  if ((int64_t)d->batch * ((int64_t)d->max_context + 1024) >= (int64_t)1 << 31)
+    return KVC_ERR_UNSUPPORTED;
   if (d->attn == KVC_ATTN_GQA) {
     if (d->n_kv_heads < 1 || d->n_heads % d->n_kv_heads != 0) return KVC_ERR_INVALID_ARG;
     if (d->latent_dim != 0 || d->rope_dim != 0) return KVC_ERR_INVALID_ARG;
     if (!valid_gqa_head_dim(d->head_dim)) return KVC_ERR_UNSUPPORTED;
+    if ((int64_t)d->max_context * d->head_dim * elem_size(d->dtype) >= (int64_t)1 << 31)
+      return KVC_ERR_UNSUPPORTED;
     return KVC_OK;
   }
   if (d->attn == KVC_ATTN_MLA) {

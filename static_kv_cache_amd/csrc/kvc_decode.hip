@@ -53,8 +53,8 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazy = 8.0f;  // log2 headroom before the running maximum is moved (VALU piece)
-constexpr float kLazyMfma = 64.0f;
-constexpr int kBufWord3 = 0x00020000;  // raw buffer resource word 3 (32-bit data format)  // the same for the matrix-core piece (fp32 sums, bf16 P)
+constexpr float kLazyMfma = 64.0f;  // the same for the matrix-core piece (fp32 sums, bf16 P)
+constexpr int kBufWord3 = 0x00020000;  // raw buffer resource word 3 (32-bit data format)
 constexpr int kWaves = 4;      // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
 
@@ -186,15 +186,30 @@ __device__ __forceinline__ int wg_of(long long x, long long R, int W) {
   return w;
 }
 
-constexpr int kMaxPiecesPerSegment = 32;  // grid cap: at most ~32 workgroups per segment
+// Start-up cost of a segment in rows: a workgroup that begins a segment
+// pays for its q load, the first tile's latency and the epilogue whatever
+// the number of rows. Each segment is given this many virtual rows in front
+// of its real ones, so a workgroup whose range crosses into another segment
+// is handed correspondingly fewer real rows and all workgroups finish
+// together. Virtual rows map to no work.
+#ifndef KVC_SEG_ROWS
+constexpr int kSegRows = 384;
+#else
+constexpr int kSegRows = KVC_SEG_ROWS;
+#endif
+static_assert(kSegRows >= 0 && kSegRows <= 1024, "row space must stay below 2^31 (see the desc limits)");
+
+constexpr int kMaxSpan = 64;              // grid cap: the longest segment spans <= kMaxSpan + 2 workgroups
+constexpr int kMaxMerge = kMaxSpan + 2;     // pieces of one segment, at most
 constexpr int kMinRowsPerWorkgroup = 64;  // and at least 64 rows each (no empty ranges)
 
 // Workgroups that share the row space: the launched grid, capped so every
-// workgroup gets >= kMinRowsPerWorkgroup rows and a segment is cut into at
-// most ~kMaxPiecesPerSegment pieces (bounds the merge of one segment).
-__device__ __forceinline__ int effective_wg(int n_wg, long long R, long long segments) {
+// workgroup gets >= kMinRowsPerWorkgroup rows and every workgroup's range
+// is at least 1/kMaxSpan of the longest segment (u_max virtual rows), so a
+// segment is cut into at most kMaxMerge pieces.
+__device__ __forceinline__ int effective_wg(int n_wg, long long R, int u_max) {
   long long w = n_wg;
-  w = min(w, max(1LL, segments * kMaxPiecesPerSegment));
+  w = min(w, max(1LL, R * kMaxSpan / max(u_max, 1)));
   w = min(w, max(1LL, R / kMinRowsPerWorkgroup));
   return (int)w;
 }
@@ -225,38 +240,70 @@ __device__ void finish_splits(const DecodeArgs& a, const SplitPiece* sp, int nsp
     s_flag[threadIdx.x * 3 + 2] = w1 - w0 + 1;
   }
   __syncthreads();
+  // Merge in two rounds of loads: every piece's (m, l) into shared memory,
+  // the weights 2^(m_p - m*) and 1/l* per head, then each thread's output
+  // elements with all of their partial loads in flight together.
+  __shared__ float s_w[kMaxMerge * 16];  // m_p, then the weight of piece p (head-minor)
+  __shared__ float s_l[kMaxMerge * 16];
+  __shared__ float s_inv[16];
   const int gc = a.chunk_heads;
-  constexpr int K = 8;  // pieces loaded together
+  constexpr int E = 2;  // output elements per thread and pass
+  constexpr int K = 8;  // pieces per batch of loads
   for (int k = 0; k < nsp; ++k) {
     if (!s_flag[k * 3]) continue;
     const SplitPiece& q = sp[k];
     const int w0 = s_flag[k * 3 + 1];
     const int np = s_flag[k * 3 + 2];
-    for (int idx = threadIdx.x; idx < gc * D; idx += kThreads) {
-      const int h = idx / D;
-      const int d = idx - h * D;
-      auto entry = [&](int p) { return ((size_t)(w0 + p + q.s)) * SH + h; };
+    auto entry = [&](int p, int h) { return ((size_t)(w0 + p + q.s)) * SH + h; };
+    for (int t = threadIdx.x; t < np * gc; t += kThreads) {
+      const int p = t / gc, h = t - p * gc;
+      s_w[t] = get(a.ws_ml + entry(p, h) * 2);
+      s_l[t] = get(a.ws_ml + entry(p, h) * 2 + 1);
+    }
+    __syncthreads();
+    if (threadIdx.x < gc) {
+      const int h = threadIdx.x;
       float mx = -INFINITY;
-      for (int p = 0; p < np; ++p) mx = fmaxf(mx, get(a.ws_ml + entry(p) * 2));
-      float x = 0.0f, lsum = 0.0f;
-      for (int p0 = 0; p0 < np; p0 += K) {
-        float mm[K], ll[K], aa[K];
+      for (int p = 0; p < np; ++p) mx = fmaxf(mx, s_w[p * gc + h]);
+      float lsum = 0.0f;
+      for (int p = 0; p < np; ++p) {
+        const float f = __builtin_amdgcn_exp2f(s_w[p * gc + h] - mx);
+        s_w[p * gc + h] = f;
+        lsum = fmaf(s_l[p * gc + h], f, lsum);
+      }
+      s_inv[h] = 1.0f / lsum;
+    }
+    __syncthreads();
+    T* o = reinterpret_cast<T*>(a.out) + ((size_t)q.b * a.n_heads + q.h0) * D;
+    for (int base = 0; base < gc * D; base += E * kThreads) {
+      float x[E];
 #pragma unroll
-        for (int i = 0; i < K; ++i) {
-          const int pc = min(p0 + i, np - 1);
-          mm[i] = get(a.ws_ml + entry(pc) * 2);
-          ll[i] = get(a.ws_ml + entry(pc) * 2 + 1);
-          aa[i] = get(a.ws_acc + entry(pc) * D + d);
+      for (int e = 0; e < E; ++e) x[e] = 0.0f;
+      for (int p0 = 0; p0 < np; p0 += K) {
+        float aa[E][K];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int idx = min(base + e * kThreads + (int)threadIdx.x, gc * D - 1);
+          const int h = idx / D, d = idx - h * D;
+#pragma unroll
+          for (int i = 0; i < K; ++i) aa[e][i] = get(a.ws_acc + entry(min(p0 + i, np - 1), h) * D + d);
         }
 #pragma unroll
-        for (int i = 0; i < K; ++i) {
-          const float f = (p0 + i < np) ? __builtin_amdgcn_exp2f(mm[i] - mx) : 0.0f;
-          x = fmaf(aa[i], f, x);
-          lsum = fmaf(ll[i], f, lsum);
+        for (int e = 0; e < E; ++e) {
+          const int idx = min(base + e * kThreads + (int)threadIdx.x, gc * D - 1);
+          const int h = idx / D;
+#pragma unroll
+          for (int i = 0; i < K; ++i)
+            if (p0 + i < np) x[e] = fmaf(aa[e][i], s_w[(p0 + i) * gc + h], x[e]);
         }
       }
-      store_out(reinterpret_cast<T*>(a.out) + ((size_t)q.b * a.n_heads + q.h0 + h) * D + d, x / lsum);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int idx = base + e * kThreads + (int)threadIdx.x;
+        if (idx < gc * D) store_out(o + idx, x[e] * s_inv[idx / D]);
+      }
     }
+    __syncthreads();  // s_w, s_l and s_inv are reused by the next merge
     if (threadIdx.x == 0) __hip_atomic_store(a.ws_cnt + q.s, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
@@ -680,14 +727,17 @@ __attribute__((amdgpu_waves_per_eu(KVC_WAVES_PER_EU, KVC_WAVES_PER_EU)))
 void gqa_decode_kernel(DecodeArgs a) {
   __shared__ typename P::Smem sm;
   __shared__ int32_t s_prefix[KVC_MAX_BATCH + 1];
+  __shared__ int32_t s_umax;  // longest segment in virtual rows
 
-  // Prefix sums of the (sanitised) valid lengths, by the first wave: 64
-  // sequences per pass, an inclusive shuffle scan within the wave and a
-  // running offset between passes; one barrier publishes them.
+  // Row space: each (sequence, head chunk) segment of sequence b spans
+  // u_b = n_b + kSegRows virtual rows (none if n_b = 0), the last n_b of
+  // them real. s_prefix holds the prefix sums of u_b, computed by the first
+  // wave: 64 sequences per pass, an inclusive shuffle scan within the wave
+  // and a running offset between passes; one barrier publishes them.
   const int B = a.batch;
   const int t = threadIdx.x;
   if (t < 64) {
-    int carry = 0;
+    int carry = 0, umax = 0;
     for (int b0 = 0; b0 < B; b0 += 64) {
       const int b = b0 + t;
       int n = 0;
@@ -696,7 +746,8 @@ void gqa_decode_kernel(DecodeArgs a) {
         n = seq_rows(a.valid_lens, a.cache_index, b, a.max_context, &bad);
         if (bad && blockIdx.x == 0) atomicOr(a.err_flag, 1);
       }
-      int x = n;
+      int x = n > 0 ? n + kSegRows : 0;
+      umax = max(umax, x);
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
         const int y = __shfl_up(x, off);
@@ -705,7 +756,12 @@ void gqa_decode_kernel(DecodeArgs a) {
       if (b < B) s_prefix[b + 1] = carry + x;
       carry += __shfl(x, 63);
     }
-    if (t == 0) s_prefix[0] = 0;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) umax = max(umax, __shfl_xor(umax, off));
+    if (t == 0) {
+      s_prefix[0] = 0;
+      s_umax = umax;
+    }
   }
   __syncthreads();
 
@@ -722,7 +778,7 @@ void gqa_decode_kernel(DecodeArgs a) {
     }
   }
 
-  const int W = effective_wg(a.n_wg, R, (long long)B * HC);
+  const int W = effective_wg(a.n_wg, R, s_umax);
   if (w >= W) return;
   long long x = wg_lo(w, R, W);
   const long long hi = wg_lo(w + 1, R, W);
@@ -739,36 +795,40 @@ void gqa_decode_kernel(DecodeArgs a) {
   }
   int b = lo_b;
   while ((long long)s_prefix[b + 1] * HC <= x) ++b;  // skip empty sequences
-  int n = s_prefix[b + 1] - s_prefix[b];
-  int hc = (int)((x - (long long)s_prefix[b] * HC) / n);
+  int u = s_prefix[b + 1] - s_prefix[b];               // virtual rows per segment of b
+  int hc = (int)((x - (long long)s_prefix[b] * HC) / u);
 
   while (x < hi) {
-    const long long seg_start = (long long)s_prefix[b] * HC + (long long)hc * n;
-    const long long seg_end = seg_start + n;
+    const long long vs = (long long)s_prefix[b] * HC + (long long)hc * u;
+    const long long real0 = vs + kSegRows;  // row-space position of the segment's row 0
+    const long long seg_end = vs + u;
     const long long piece_end = seg_end < hi ? seg_end : hi;
-    const int r_begin = (int)(x - seg_start);
-    const int r_end = (int)(piece_end - seg_start);
-    const long long s = (long long)b * HC + hc;
-    const bool whole = r_begin == 0 && r_end == n;
-    const int kvg = hc / a.head_chunks;
-    const int chunk = hc % a.head_chunks;
-    P::run(a, sm, b, kvg, chunk, r_begin, r_end, whole, (long long)w + s);
-    if (!whole && nsplit < 2) {
-      if (threadIdx.x == 0) {  // read after the barriers in finish_splits
-        split[nsplit].s = s;
-        split[nsplit].seg_start = seg_start;
-        split[nsplit].n = n;
-        split[nsplit].b = b;
-        split[nsplit].h0 = kvg * (a.n_heads / a.n_kv_heads) + chunk * a.chunk_heads;
+    const int n = u - kSegRows;
+    const int r_begin = x > real0 ? (int)(x - real0) : 0;
+    const int r_end = piece_end > real0 ? (int)(piece_end - real0) : 0;
+    if (r_end > r_begin) {  // else the range only touches the segment's virtual rows
+      const long long s = (long long)b * HC + hc;
+      const bool whole = r_begin == 0 && r_end == n;
+      const int kvg = hc / a.head_chunks;
+      const int chunk = hc % a.head_chunks;
+      P::run(a, sm, b, kvg, chunk, r_begin, r_end, whole, (long long)w + s);
+      if (!whole && nsplit < 2) {
+        if (threadIdx.x == 0) {  // read after the barriers in finish_splits
+          split[nsplit].s = s;
+          split[nsplit].seg_start = real0;
+          split[nsplit].n = n;
+          split[nsplit].b = b;
+          split[nsplit].h0 = kvg * (a.n_heads / a.n_kv_heads) + chunk * a.chunk_heads;
+        }
+        ++nsplit;
       }
-      ++nsplit;
     }
     x = piece_end;
     if (x >= hi) break;
     if (++hc == HC) {  // next sequence with rows
       hc = 0;
       do { ++b; } while (s_prefix[b + 1] == s_prefix[b]);
-      n = s_prefix[b + 1] - s_prefix[b];
+      u = s_prefix[b + 1] - s_prefix[b];
     }
   }
   if (nsplit > 0)

@@ -245,6 +245,24 @@ def test_fewer_rows_than_workgroups(workgroups):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_skewed_lengths_many_pieces(dtype):
+    """One full-length sequence among many of one to three rows, with the
+    largest grid: the long segment is cut into the most pieces the grid cap
+    allows (about 65), all merged by the last one to arrive."""
+    dev = device()
+    B, H, Hkv, D, S = 64, 8, 1, 128, 4096
+    valid = np.array([S] + [1 + i % 3 for i in range(B - 1)], dtype=np.int32)
+    case = synthetic.random_gqa_case(79, B, H, Hkv, D, S, dtype, valid_lens=valid)
+    cache = kvc.Cache(kvc.gqa_desc(1, B, H, Hkv, D, S, dtype))
+    wg = cache.workgroups()[1]
+    cache.free()
+    say(f"skewed lengths: {dtype} workgroups={wg}")
+    cache, ref, out, want = run_case(dev, case, workgroups=wg, dtype=dtype)
+    tol_check(to_f64(out), want, dtype, "skewed")
+    cache.free()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_single_row_is_exact(dtype):
     """n = 1: softmax of one logit is exactly 1, so out = V row 0 bit for bit."""
     dev = device()
