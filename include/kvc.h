@@ -71,7 +71,8 @@ typedef enum { KVC_ATTN_GQA = 0, KVC_ATTN_MLA = 1 } kvc_attn;
  *       latent_dim = rope_dim = 0.
  *       Layout: [n_layers][2 (K, V)][batch][n_kv_heads][max_context][head_dim].
  *  MLA: n_kv_heads = 1; latent_dim = 512, rope_dim = 64, head_dim = 128
- *       (per-head width of q_nope and of the output), bf16 only.
+ *       (per-head width of q_nope and of the output), bf16 only;
+ *       n_heads <= 16 or a multiple of 16.
  *       Layout: [n_layers][batch][max_context][latent_dim + rope_dim], each
  *       row = latent c (latent_dim) then the rotary key kR (rope_dim).
  *  Group of query head h: kv head h / (n_heads / n_kv_heads) (contiguous). */
@@ -84,8 +85,8 @@ typedef struct {
   int32_t n_kv_heads;   /* H_kv */
   int32_t head_dim;     /* d_h */
   int32_t max_context;  /* S >= 1, rows per sequence; KVC_ERR_UNSUPPORTED when
-                           batch * (S + 1024) >= 2^31 or one (sequence, kv
-                           head) block S * head_dim * p >= 2^31 bytes */
+                           batch * (S + 1024) >= 2^31 or the rows of one
+                           (sequence, kv head) take >= 2^30 bytes */
   int32_t latent_dim;   /* MLA d_c */
   int32_t rope_dim;     /* MLA d_R */
 } kvc_desc;

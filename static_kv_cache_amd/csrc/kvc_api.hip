@@ -39,7 +39,7 @@ kvc_status validate_desc(const kvc_desc* d) {
     if (d->n_kv_heads < 1 || d->n_heads % d->n_kv_heads != 0) return KVC_ERR_INVALID_ARG;
     if (d->latent_dim != 0 || d->rope_dim != 0) return KVC_ERR_INVALID_ARG;
     if (!valid_gqa_head_dim(d->head_dim)) return KVC_ERR_UNSUPPORTED;
-    if ((int64_t)d->max_context * d->head_dim * elem_size(d->dtype) >= (int64_t)1 << 31)
+    if ((int64_t)d->max_context * d->head_dim * elem_size(d->dtype) >= (int64_t)1 << 30)
       return KVC_ERR_UNSUPPORTED;
     return KVC_OK;
   }
@@ -47,6 +47,9 @@ kvc_status validate_desc(const kvc_desc* d) {
     if (d->n_kv_heads != 1) return KVC_ERR_INVALID_ARG;
     if (d->latent_dim < 1 || d->rope_dim < 0 || d->head_dim < 1) return KVC_ERR_INVALID_ARG;
     if (d->dtype != KVC_BF16 || d->latent_dim != 512 || d->rope_dim != 64 || d->head_dim != 128)
+      return KVC_ERR_UNSUPPORTED;
+    if (d->n_heads > 16 && d->n_heads % 16 != 0) return KVC_ERR_UNSUPPORTED;  // chunks of 16 heads
+    if ((int64_t)d->max_context * (d->latent_dim + d->rope_dim) * elem_size(d->dtype) >= (int64_t)1 << 30)
       return KVC_ERR_UNSUPPORTED;
     return KVC_OK;
   }
@@ -117,7 +120,6 @@ kvc_status kvc_alloc(const kvc_desc* desc, void* external, kvc_cache** out) {
   *out = nullptr;
   kvc_status s = validate_desc(desc);
   if (s != KVC_OK) return s;
-  if (desc->attn == KVC_ATTN_MLA) return KVC_ERR_UNSUPPORTED;  // latent kernels not built yet
   if (external && ((uintptr_t)external % 256) != 0) return KVC_ERR_INVALID_ARG;
   uint64_t bytes = 0;
   s = bytes_of(desc, &bytes);

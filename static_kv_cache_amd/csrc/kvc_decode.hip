@@ -47,15 +47,19 @@
 
 #include <type_traits>
 
-#include "kvc_internal.h"
+#include "kvc_device.h"
 
 namespace {
 
-constexpr float kLog2e = 1.4426950408889634f;
+using namespace kvcd;
+
 constexpr float kLazy = 8.0f;  // log2 headroom before the running maximum is moved (VALU piece)
 constexpr float kLazyMfma = 64.0f;  // the same for the matrix-core piece (fp32 sums, bf16 P)
-constexpr int kBufWord3 = 0x00020000;  // raw buffer resource word 3 (32-bit data format)
+#ifndef KVC_WAVES
 constexpr int kWaves = 4;      // waves per workgroup
+#else
+constexpr int kWaves = KVC_WAVES;
+#endif
 constexpr int kThreads = 64 * kWaves;
 
 template <typename T>
@@ -64,8 +68,6 @@ template <>
 struct Storage<float> {  // fp32: 4 elements per 16-byte vector
   static constexpr int kEPV = 4;
 };
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // Cross-lane move within a row of 16 lanes. All patterns used here are
 // permutations, so every source lane is valid; bound_ctrl lets the compiler
@@ -124,40 +126,6 @@ __device__ __forceinline__ void vec_unpack(const uint4& v, float (&f)[4], float)
   f[3] = __uint_as_float(v.w);
 }
 
-// fp32 -> bf16 bits, round to nearest, ties to even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint16_t bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x0040u);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-__device__ __forceinline__ void store_out(uint16_t* p, float f) { *p = bf16_rne(f); }
-__device__ __forceinline__ void store_out(float* p, float f) { *p = f; }
-
-// Valid rows of sequence b as the kernels use them: out-of-range lengths
-// count as 0 (the sequence is skipped and flagged).
-__device__ __forceinline__ int seq_rows(const int32_t* valid_lens, const int32_t* cache_index, int b,
-                                        int max_context, bool* bad) {
-  const int n = valid_lens ? valid_lens[b] : cache_index[b] + 1;
-  *bad = n < 0 || n > max_context;
-  return *bad ? 0 : n;
-}
-
-// Partials are exchanged between workgroups that may sit on different XCDs
-// (each with its own L2). They are written and read with device-scope
-// relaxed atomic accesses (global_store/load ... sc1), which are coherent at
-// device scope per location; a writer waits for its stores to complete
-// (vmcnt(0)) before it counts itself in, and the last arrival reads them
-// back. This avoids the full-L2 writeback/invalidate of a device-scope fence.
-__device__ __forceinline__ void put(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float get(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// s_waitcnt vmcnt(0) (expcnt, lgkmcnt left alone): this thread's stores are done
-__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
 struct DecodeArgs {
   const void* k;               // layer keys   [B][H_kv][S][D]
   const void* v;               // layer values [B][H_kv][S][D]
@@ -176,16 +144,6 @@ struct DecodeArgs {
   int32_t* err_flag;
 };
 
-__device__ __forceinline__ long long wg_lo(int w, long long R, int W) { return (long long)w * R / W; }
-
-// Workgroup whose row range contains row x of the row space.
-__device__ __forceinline__ int wg_of(long long x, long long R, int W) {
-  int w = (int)(x * W / R);
-  while (w + 1 < W && wg_lo(w + 1, R, W) <= x) ++w;
-  while (w > 0 && wg_lo(w, R, W) > x) --w;
-  return w;
-}
-
 // Start-up cost of a segment in rows: a workgroup that begins a segment
 // pays for its q load, the first tile's latency and the epilogue whatever
 // the number of rows. Each segment is given this many virtual rows in front
@@ -197,22 +155,7 @@ constexpr int kSegRows = 384;
 #else
 constexpr int kSegRows = KVC_SEG_ROWS;
 #endif
-static_assert(kSegRows >= 0 && kSegRows <= 1024, "row space must stay below 2^31 (see the desc limits)");
-
-constexpr int kMaxSpan = 64;              // grid cap: the longest segment spans <= kMaxSpan + 2 workgroups
-constexpr int kMaxMerge = kMaxSpan + 2;     // pieces of one segment, at most
-constexpr int kMinRowsPerWorkgroup = 64;  // and at least 64 rows each (no empty ranges)
-
-// Workgroups that share the row space: the launched grid, capped so every
-// workgroup gets >= kMinRowsPerWorkgroup rows and every workgroup's range
-// is at least 1/kMaxSpan of the longest segment (u_max virtual rows), so a
-// segment is cut into at most kMaxMerge pieces.
-__device__ __forceinline__ int effective_wg(int n_wg, long long R, int u_max) {
-  long long w = n_wg;
-  w = min(w, max(1LL, R * kMaxSpan / max(u_max, 1)));
-  w = min(w, max(1LL, R / kMinRowsPerWorkgroup));
-  return (int)w;
-}
+static_assert(kSegRows >= 0 && kSegRows <= kMaxSegRows, "row space must stay below 2^31");
 
 // A piece that is part of a segment (only a workgroup's first and last
 // piece can be) is recorded while the workgroup streams on; at the end the
@@ -508,11 +451,7 @@ struct ValuPiece {
   }
 };
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // bf16 piece on the matrix cores (see the file comment). Lane l of a wave is
 // (g, j) = (l / 16, l % 16). MFMA 16x16x32: A lane holds A[j][8g..8g+7],
@@ -554,6 +493,7 @@ struct MfmaPiece {
     const int g = lane >> 4;
     const int j = lane & 15;
     const int gc = a.chunk_heads;
+
     const int h0 = kvg * (a.n_heads / a.n_kv_heads) + chunk * gc;
     const float scale_log2 = a.scale_log2;
 
@@ -729,41 +669,10 @@ void gqa_decode_kernel(DecodeArgs a) {
   __shared__ int32_t s_prefix[KVC_MAX_BATCH + 1];
   __shared__ int32_t s_umax;  // longest segment in virtual rows
 
-  // Row space: each (sequence, head chunk) segment of sequence b spans
-  // u_b = n_b + kSegRows virtual rows (none if n_b = 0), the last n_b of
-  // them real. s_prefix holds the prefix sums of u_b, computed by the first
-  // wave: 64 sequences per pass, an inclusive shuffle scan within the wave
-  // and a running offset between passes; one barrier publishes them.
   const int B = a.batch;
   const int t = threadIdx.x;
-  if (t < 64) {
-    int carry = 0, umax = 0;
-    for (int b0 = 0; b0 < B; b0 += 64) {
-      const int b = b0 + t;
-      int n = 0;
-      if (b < B) {
-        bool bad;
-        n = seq_rows(a.valid_lens, a.cache_index, b, a.max_context, &bad);
-        if (bad && blockIdx.x == 0) atomicOr(a.err_flag, 1);
-      }
-      int x = n > 0 ? n + kSegRows : 0;
-      umax = max(umax, x);
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(x, off);
-        x += (t >= off) ? y : 0;
-      }
-      if (b < B) s_prefix[b + 1] = carry + x;
-      carry += __shfl(x, 63);
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) umax = max(umax, __shfl_xor(umax, off));
-    if (t == 0) {
-      s_prefix[0] = 0;
-      s_umax = umax;
-    }
-  }
-  __syncthreads();
+  build_row_space(a.valid_lens, a.cache_index, B, a.max_context, kSegRows, s_prefix, &s_umax, a.err_flag,
+                  blockIdx.x == 0);
 
   const int HC = a.n_kv_heads * a.head_chunks;  // segments per sequence
   const long long R = (long long)s_prefix[B] * HC;
@@ -787,50 +696,24 @@ void gqa_decode_kernel(DecodeArgs a) {
   __shared__ SplitPiece split[2];  // a workgroup's first and last piece may be parts of segments
   int nsplit = 0;
 
-  // first segment holding row x: sequence by binary search, then head chunk
-  int lo_b = 0, hi_b = B - 1;
-  while (lo_b < hi_b) {
-    const int mid = (lo_b + hi_b + 1) >> 1;
-    if ((long long)s_prefix[mid] * HC <= x) lo_b = mid; else hi_b = mid - 1;
-  }
-  int b = lo_b;
-  while ((long long)s_prefix[b + 1] * HC <= x) ++b;  // skip empty sequences
-  int u = s_prefix[b + 1] - s_prefix[b];               // virtual rows per segment of b
-  int hc = (int)((x - (long long)s_prefix[b] * HC) / u);
-
-  while (x < hi) {
-    const long long vs = (long long)s_prefix[b] * HC + (long long)hc * u;
-    const long long real0 = vs + kSegRows;  // row-space position of the segment's row 0
-    const long long seg_end = vs + u;
-    const long long piece_end = seg_end < hi ? seg_end : hi;
-    const int n = u - kSegRows;
-    const int r_begin = x > real0 ? (int)(x - real0) : 0;
-    const int r_end = piece_end > real0 ? (int)(piece_end - real0) : 0;
-    if (r_end > r_begin) {  // else the range only touches the segment's virtual rows
-      const long long s = (long long)b * HC + hc;
-      const bool whole = r_begin == 0 && r_end == n;
-      const int kvg = hc / a.head_chunks;
-      const int chunk = hc % a.head_chunks;
-      P::run(a, sm, b, kvg, chunk, r_begin, r_end, whole, (long long)w + s);
-      if (!whole && nsplit < 2) {
-        if (threadIdx.x == 0) {  // read after the barriers in finish_splits
-          split[nsplit].s = s;
-          split[nsplit].seg_start = real0;
-          split[nsplit].n = n;
-          split[nsplit].b = b;
-          split[nsplit].h0 = kvg * (a.n_heads / a.n_kv_heads) + chunk * a.chunk_heads;
-        }
-        ++nsplit;
+  for_each_piece(s_prefix, B, HC, kSegRows, x, hi,
+                 [&](int b, int hc, int r_begin, int r_end, int n, long long real0) {
+    const long long s = (long long)b * HC + hc;
+    const bool whole = r_begin == 0 && r_end == n;
+    const int kvg = hc / a.head_chunks;
+    const int chunk = hc % a.head_chunks;
+    P::run(a, sm, b, kvg, chunk, r_begin, r_end, whole, (long long)w + s);
+    if (!whole && nsplit < 2) {
+      if (threadIdx.x == 0) {  // read after the barriers in finish_splits
+        split[nsplit].s = s;
+        split[nsplit].seg_start = real0;
+        split[nsplit].n = n;
+        split[nsplit].b = b;
+        split[nsplit].h0 = kvg * (a.n_heads / a.n_kv_heads) + chunk * a.chunk_heads;
       }
+      ++nsplit;
     }
-    x = piece_end;
-    if (x >= hi) break;
-    if (++hc == HC) {  // next sequence with rows
-      hc = 0;
-      do { ++b; } while (s_prefix[b + 1] == s_prefix[b]);
-      u = s_prefix[b + 1] - s_prefix[b];
-    }
-  }
+  });
   if (nsplit > 0)
     finish_splits<typename P::Elem, P::kD, P::kSlotHeads>(a, split, nsplit, s_flag, R, W);
 }

@@ -1,0 +1,171 @@
+// Device-side pieces shared by the attention kernels (GQA and latent):
+// vector types, bf16 rounding, the row space that the persistent grid splits,
+// and the device-coherent accesses used to hand partials between workgroups.
+// Internal to libkvc.so.
+#pragma once
+
+#include <math.h>
+#include <stdint.h>
+
+#include "kvc_internal.h"
+
+namespace kvcd {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kBufWord3 = 0x00020000;  // raw buffer resource word 3 (32-bit data format)
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// fp32 -> bf16 bits, round to nearest, ties to even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x0040u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ void store_out(uint16_t* p, float f) { *p = bf16_rne(f); }
+__device__ __forceinline__ void store_out(float* p, float f) { *p = f; }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// Valid rows of sequence b as the kernels use them: out-of-range lengths
+// count as 0 (the sequence is skipped and flagged).
+__device__ __forceinline__ int seq_rows(const int32_t* valid_lens, const int32_t* cache_index, int b,
+                                        int max_context, bool* bad) {
+  const int n = valid_lens ? valid_lens[b] : cache_index[b] + 1;
+  *bad = n < 0 || n > max_context;
+  return *bad ? 0 : n;
+}
+
+// Partials handed between workgroups of one kernel, which may sit on
+// different XCDs (each with its own L2), are written and read with
+// device-scope relaxed atomic accesses (global_store/load ... sc1): coherent
+// at device scope per location. A writer waits for its stores to complete
+// (vmcnt(0)) before it counts itself in, and the last arrival reads them
+// back. This avoids the full-L2 writeback/invalidate of a device-scope fence.
+__device__ __forceinline__ void put(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float get(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// s_waitcnt vmcnt(0) (expcnt, lgkmcnt left alone): this thread's stores are done
+__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// ---- the row space ---------------------------------------------------------
+//
+// A "segment" is the valid rows [0, n_b) of one (sequence, head chunk) pair
+// (for GQA the chunk runs over kv heads and query-head chunks; for the
+// latent cache over query-head chunks). The HC segments of sequence b are
+// laid end to end in one row space, each taking u_b = n_b + seg_rows
+// virtual rows (none if n_b = 0) of which the last n_b are real: seg_rows
+// stands for the fixed start-up cost of a segment (query load, the first
+// tile's latency, the epilogue), so a workgroup whose range crosses into a
+// new segment is handed correspondingly fewer real rows. Workgroup w of W
+// takes rows [w R / W, (w + 1) R / W); the part of a segment inside one
+// workgroup is a "piece".
+
+__device__ __forceinline__ long long wg_lo(int w, long long R, int W) { return (long long)w * R / W; }
+
+// Workgroup whose row range contains row x of the row space.
+__device__ __forceinline__ int wg_of(long long x, long long R, int W) {
+  int w = (int)(x * W / R);
+  while (w + 1 < W && wg_lo(w + 1, R, W) <= x) ++w;
+  while (w > 0 && wg_lo(w, R, W) > x) --w;
+  return w;
+}
+
+constexpr int kMaxSpan = 64;               // the longest segment spans <= kMaxSpan + 2 workgroups
+constexpr int kMaxMerge = kMaxSpan + 2;    // pieces of one segment, at most
+constexpr int kMinRowsPerWorkgroup = 64;   // and every workgroup gets >= 64 rows (no empty ranges)
+constexpr int kMaxSegRows = 1024;          // start-up rows allowed (the desc limits keep R < 2^31)
+
+// Workgroups that share the row space: the launched grid, capped so every
+// workgroup gets >= kMinRowsPerWorkgroup rows and every workgroup's range
+// is at least 1/kMaxSpan of the longest segment (u_max virtual rows), so a
+// segment is cut into at most kMaxMerge pieces.
+__device__ __forceinline__ int effective_wg(int n_wg, long long R, int u_max) {
+  long long w = n_wg;
+  w = min(w, max(1LL, R * kMaxSpan / max(u_max, 1)));
+  w = min(w, max(1LL, R / kMinRowsPerWorkgroup));
+  return (int)w;
+}
+
+// Prefix sums s_prefix[0..B] of u_b and the largest u_b, by the first wave
+// (64 sequences per pass, an inclusive shuffle scan within the wave and a
+// running offset between passes); ends with a barrier that publishes them.
+// Every thread of the workgroup must call it. Out-of-range lengths raise
+// *err_flag when flag_errors is set.
+__device__ __forceinline__ void build_row_space(const int32_t* valid_lens, const int32_t* cache_index, int B,
+                                                int max_context, int seg_rows, int32_t* s_prefix,
+                                                int32_t* s_umax, int32_t* err_flag, bool flag_errors) {
+  const int t = threadIdx.x;
+  if (t < 64) {
+    int carry = 0, umax = 0;
+    for (int b0 = 0; b0 < B; b0 += 64) {
+      const int b = b0 + t;
+      int n = 0;
+      if (b < B) {
+        bool bad;
+        n = seq_rows(valid_lens, cache_index, b, max_context, &bad);
+        if (bad && flag_errors) atomicOr(err_flag, 1);
+      }
+      int x = n > 0 ? n + seg_rows : 0;
+      umax = max(umax, x);
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off);
+        x += (t >= off) ? y : 0;
+      }
+      if (b < B) s_prefix[b + 1] = carry + x;
+      carry += __shfl(x, 63);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) umax = max(umax, __shfl_xor(umax, off));
+    if (t == 0) {
+      s_prefix[0] = 0;
+      *s_umax = umax;
+    }
+  }
+  __syncthreads();
+}
+
+// Calls f(b, hc, r_begin, r_end, n, real0) for every piece of the row range
+// [x, hi): rows [r_begin, r_end) (r_end > r_begin) of segment (b, hc), whose
+// n real rows start at row-space position real0.
+template <class F>
+__device__ __forceinline__ void for_each_piece(const int32_t* s_prefix, int B, int HC, int seg_rows,
+                                               long long x, long long hi, F&& f) {
+  // first segment holding row x: sequence by binary search, then head chunk
+  int lo_b = 0, hi_b = B - 1;
+  while (lo_b < hi_b) {
+    const int mid = (lo_b + hi_b + 1) >> 1;
+    if ((long long)s_prefix[mid] * HC <= x) lo_b = mid; else hi_b = mid - 1;
+  }
+  int b = lo_b;
+  while ((long long)s_prefix[b + 1] * HC <= x) ++b;  // skip empty sequences
+  int u = s_prefix[b + 1] - s_prefix[b];               // virtual rows per segment of b
+  int hc = (int)((x - (long long)s_prefix[b] * HC) / u);
+  while (x < hi) {
+    const long long vs = (long long)s_prefix[b] * HC + (long long)hc * u;
+    const long long real0 = vs + seg_rows;
+    const long long seg_end = vs + u;
+    const long long piece_end = seg_end < hi ? seg_end : hi;
+    const int n = u - seg_rows;
+    const int r_begin = x > real0 ? (int)(x - real0) : 0;
+    const int r_end = piece_end > real0 ? (int)(piece_end - real0) : 0;
+    if (r_end > r_begin) f(b, hc, r_begin, r_end, n, real0);  // else only virtual rows
+    x = piece_end;
+    if (x >= hi) break;
+    if (++hc == HC) {  // next sequence with rows
+      hc = 0;
+      do { ++b; } while (s_prefix[b + 1] == s_prefix[b]);
+      u = s_prefix[b + 1] - s_prefix[b];
+    }
+  }
+}
+
+}  // namespace kvcd

@@ -1,15 +1,448 @@
-// Latent (MLA) decode kernels. Not built yet: every launcher reports
-// "not supported", and kvc_alloc refuses MLA descriptors before reaching them.
-#include "kvc_internal.h"
+// Latent (MLA) decode over the static latent cache.
+//
+// What is computed ("10.3 - KV cache implementation details", section 4.3;
+// "KV-Cache Mechanics", the MHA / GQA / MLA comparison and its "absorb"
+// overhead): every cached row holds the latent c_j (d_c = 512) followed by
+// the rotary key kR_j (d_R = 64), shared by all query heads. For query head
+// h of sequence b with n = n_b valid rows,
+//     q~[b,h]  = [ W_UK[h]^T q_nope[b,h] ; q_rope[b,h] ]          (absorb)
+//     o~[b,h]  = softmax(sm_scale * R[b,0:n] q~[b,h]) R[b,0:n,0:d_c]  (latent attention)
+//     out[b,h] = W_UV[h]^T o~[b,h]                                  (up-projection)
+// which equals attention with per-head keys [W_UK[h] c_j ; kR_j] and values
+// W_UV[h]^T c_j (associativity). Rows at or past n are never loaded.
+//
+// How:
+//  - Latent attention is the part that reads the cache, and it is a dense
+//    contraction (16 heads x 576 dims per row against every row), so it runs
+//    on the matrix cores. Work space as for GQA (row space of segments =
+//    (sequence, chunk of up to 16 heads), persistent grid, pieces). A
+//    workgroup streams its rows in tiles of 32 rows (36 KB, one contiguous
+//    block) staged through a skewed LDS tile; the next tile is in flight in
+//    registers while the current one is used. The latent rows are read from
+//    HBM once for all heads of the chunk.
+//  - Every wave computes the whole score tile S = R_tile q~^T
+//    (v_mfma_f32_16x16x32_bf16, 18 steps of 32 dims, rows as the A operand
+//    read from LDS, the heads as the B operand held in registers), so every
+//    wave holds identical softmax state and no exchange is needed; then
+//    each wave applies P to its own quarter (128) of the 512 latent columns
+//    (v_mfma_f32_16x16x16_bf16 with the rows reaching the B operand through
+//    ds_read_b64_tr_b16).
+//  - Every piece writes its partial (o~ / l as bf16, m and l as fp32) to
+//    slot w + s; a second kernel merges the pieces of each (sequence, head)
+//    with weights 2^(m_p - m*) l_p / l*. A latent partial is 16 x 512 wide,
+//    too wide for one workgroup to merge at the end of the streaming kernel.
+//  - The absorb and up-projection are small batched products over the
+//    weights (2 MB each), done with fp32 FMAs on the vector units.
 
-hipError_t kvc_launch_mla_attn(const kvc_cache*, const void*, const void*, void*, const int32_t*,
-                               const int32_t*, float, hipStream_t) {
-  return hipErrorNotSupported;
+#include "kvc_device.h"
+
+namespace {
+
+using namespace kvcd;
+
+constexpr int kDc = 512;                     // latent width
+constexpr int kDr = 64;                      // rotary key width
+constexpr int kRow = kDc + kDr;              // elements per cached row
+constexpr int kRowBytes = 2 * kRow;          // 1152
+constexpr int kTok = 32;                     // rows per tile
+constexpr int kStride = kRowBytes + 16;      // LDS bytes per staged row (skew: conflict-free reads)
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kCols = kDc / kWaves;          // latent columns per wave in p.v (128)
+constexpr int kNB = kCols / 16;              // output column blocks per wave
+constexpr int kKS = kRow / 32;               // q.k steps of 32 dims
+constexpr int kVec = kTok * kRowBytes / 16 / kThreads;  // staged 16-byte vectors per thread per tile
+constexpr int kRowVecs = kRowBytes / 16;     // 72
+constexpr int kSlotHeads = 16;               // partial entries per workspace slot
+constexpr int kSegRowsMla = 160;             // start-up rows of a segment (see kvc_device.h)
+constexpr float kLazyMfma = 64.0f;           // log2 headroom before the reference maximum moves
+static_assert(kTok * kRowBytes % (16 * kThreads) == 0, "tile must split evenly over the threads");
+static_assert(kSegRowsMla <= kMaxSegRows, "row space must stay below 2^31");
+
+struct MlaArgs {
+  const uint16_t* rows;        // layer rows [B][S][576]
+  const uint16_t* q_abs;       // absorbed queries [B][H][576]
+  uint16_t* part;              // [slot][16][512] partial o~ / l (bf16)
+  float* ml;                   // [slot][16][2]  m (log2 units), l
+  uint16_t* out;               // merged latent output [B][H][512]
+  const int32_t* valid_lens;   // [B] or null
+  const int32_t* cache_index;  // [B] or null
+  float scale_log2;
+  int batch, n_heads, max_context;
+  int head_chunks, chunk_heads;  // H = head_chunks * chunk_heads, chunk_heads <= 16
+  int n_wg;
+  int32_t* err_flag;
+};
+
+// Rows [r_begin, r_end) of sequence b against heads [hc * gc, (hc + 1) * gc).
+__device__ __forceinline__ void mla_piece(const MlaArgs& a, unsigned char* tile, int b, int hc, int r_begin,
+                                          int r_end, long long slot) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 4;
+  const int j = lane & 15;
+  const int gc = a.chunk_heads;
+  const int h0 = hc * gc;
+  const float scale_log2 = a.scale_log2;
+
+  // q~ as the B operand: column j is head h0 + j, zero past the chunk
+  bf16x8_t qb[kKS];
+  const bool real = j < gc;
+  const uint16_t* qh = a.q_abs + ((size_t)b * a.n_heads + h0 + (real ? j : 0)) * kRow;
+#pragma unroll
+  for (int k = 0; k < kKS; ++k) {
+    u32x4_t v = *reinterpret_cast<const u32x4_t*>(qh + 32 * k + 8 * g);
+    v = real ? v : u32x4_t{0u, 0u, 0u, 0u};
+    qb[k] = __builtin_bit_cast(bf16x8_t, v);
+  }
+
+  f32x4_t o[kNB];
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb) o[nb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  float m = -INFINITY;  // reference maximum of head column j (log2 units)
+  float l = 0.0f;       // this lane's share of column j's denominator
+
+  // The resource spans exactly rows [0, r_end) of the sequence: loads past
+  // the end (the tail of the last tile, the prefetch after it) return zeros
+  // without touching memory, and their scores are masked.
+  const uint16_t* seq = a.rows + (size_t)b * a.max_context * kRow;
+  const __amdgpu_buffer_rsrc_t res = __builtin_amdgcn_make_buffer_rsrc((void*)seq, 0, r_end * kRowBytes, kBufWord3);
+  u32x4_t st[kVec];
+  auto load = [&](int t0) {
+    const int off = t0 * kRowBytes + (int)threadIdx.x * 16;
+#pragma unroll
+    for (int i = 0; i < kVec; ++i) st[i] = __builtin_amdgcn_raw_buffer_load_b128(res, off + i * 16 * kThreads, 0, 0);
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int i = 0; i < kVec; ++i) {
+      const int f = (int)threadIdx.x + i * kThreads;
+      *reinterpret_cast<u32x4_t*>(tile + (f / kRowVecs) * kStride + (f % kRowVecs) * 16) = st[i];
+    }
+  };
+
+  load(r_begin);
+  for (int t0 = r_begin; t0 < r_end; t0 += kTok) {
+    __syncthreads();  // every wave is done with the previous tile
+    stage();
+    load(t0 + kTok);  // next tile in flight while this one is used
+    __syncthreads();  // the tile is visible
+
+    // scores of two 16-row blocks: s[tb][t] = R[t0 + 16 tb + 4g + t] . q~[head j]
+    f32x4_t s[2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      s[tb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      const unsigned char* arow = tile + (16 * tb + j) * kStride + 16 * g;
+#pragma unroll
+      for (int k = 0; k < kKS; ++k) {
+        const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(arow + 64 * k);
+        s[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qb[k], s[tb], 0, 0, 0);
+      }
+    }
+    if (t0 + kTok > r_end) {
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) s[tb][t] = (t0 + 16 * tb + 4 * g + t < r_end) ? s[tb][t] : -INFINITY;
+    }
+    // online softmax with a lazily moved reference maximum (p <= 2^kLazyMfma)
+    float cand = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                       fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3]))) * scale_log2;
+    if (__builtin_amdgcn_ballot_w64(cand > m + kLazyMfma)) {
+      float mt = fmaxf(cand, __shfl_xor(cand, 16));
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      const float mn = fmaxf(m, mt);
+      const float c = __builtin_amdgcn_exp2f(m - ((mn == -INFINITY) ? 0.0f : mn));
+      l *= c;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float ct = __shfl(c, 4 * g + t);  // factor of output row (head) 4g + t
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb) o[nb][t] *= ct;
+      }
+      m = mn;
+    }
+    const float nm = (m == -INFINITY) ? 0.0f : -m;
+    s16x4_t pa[2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[tb][t], scale_log2, nm));
+        l += p;
+        pa[tb][t] = __builtin_bit_cast(short, (__bf16)p);
+      }
+    // p.v over this wave's latent columns [128 wave, 128 wave + 128)
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const unsigned char* vrow = tile + (16 * tb + 4 * g + (j >> 2)) * kStride + 2 * kCols * wave + 8 * (j & 3);
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb) {
+        const s16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4_t*)(vrow + 32 * nb));
+        o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa[tb], vb, o[nb], 0, 0, 0);
+      }
+    }
+  }
+
+  // denominators of the head columns, then the partial o~ / l, m and l
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int hr = 4 * g + t;
+    const float lr = __shfl(l, hr);
+    if (hr < gc) {
+      const float inv = 1.0f / lr;  // lr >= 1: the piece has a live row
+      uint16_t* dst = a.part + ((size_t)slot * kSlotHeads + hr) * kDc + kCols * wave + j;
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb) dst[16 * nb] = bf16_rne(o[nb][t] * inv);
+    }
+  }
+  if (wave == 0 && g == 0 && j < gc) {
+    a.ml[((size_t)slot * kSlotHeads + j) * 2] = m;
+    a.ml[((size_t)slot * kSlotHeads + j) * 2 + 1] = l;
+  }
+  __syncthreads();  // the tile is reused by the next piece
 }
-hipError_t kvc_launch_mla_absorb(const kvc_cache*, const void*, const void*, const void*, uint16_t*,
-                                 hipStream_t) {
-  return hipErrorNotSupported;
+
+// Persistent latent attention: grid = W workgroups of 256 threads.
+__global__ __launch_bounds__(kThreads) void mla_split_kernel(MlaArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char tile[kTok * kStride];
+  __shared__ int32_t s_prefix[KVC_MAX_BATCH + 1];
+  __shared__ int32_t s_umax;
+  const int B = a.batch;
+  build_row_space(a.valid_lens, a.cache_index, B, a.max_context, kSegRowsMla, s_prefix, &s_umax, a.err_flag,
+                  blockIdx.x == 0);
+  const int HC = a.head_chunks;
+  const long long R = (long long)s_prefix[B] * HC;
+  const int W = effective_wg(a.n_wg, R, s_umax);
+  const int w = blockIdx.x;
+  if (w >= W) return;
+  const long long x = wg_lo(w, R, W);
+  const long long hi = wg_lo(w + 1, R, W);
+  if (x >= hi) return;
+  for_each_piece(s_prefix, B, HC, kSegRowsMla, x, hi,
+                 [&](int b, int hc, int r_begin, int r_end, int, long long) {
+                   mla_piece(a, tile, b, hc, r_begin, r_end, (long long)w + (long long)b * HC + hc);
+                 });
 }
-hipError_t kvc_launch_mla_uproj(const kvc_cache*, const uint16_t*, const void*, void*, hipStream_t) {
-  return hipErrorNotSupported;
+
+// Merge of the pieces of segment (b, hc) for latent columns [64 y, 64 y + 64):
+// grid (B * HC, 8), 256 threads = 16 heads x 16 threads of 4 columns.
+// The partition is recomputed exactly as the split kernel made it.
+constexpr int kMergeCols = 64;
+__global__ __launch_bounds__(kThreads) void mla_merge_kernel(MlaArgs a) {
+  __shared__ int32_t s_prefix[KVC_MAX_BATCH + 1];
+  __shared__ int32_t s_umax;
+  __shared__ float s_w[kMaxMerge * kSlotHeads];  // m_p, then the weight of piece p (head-minor)
+  __shared__ float s_l[kMaxMerge * kSlotHeads];
+  const int B = a.batch;
+  build_row_space(a.valid_lens, a.cache_index, B, a.max_context, kSegRowsMla, s_prefix, &s_umax, a.err_flag,
+                  false);
+  const int HC = a.head_chunks;
+  const int gc = a.chunk_heads;
+  const int seg = blockIdx.x;
+  const int b = seg / HC;
+  const int hc = seg - b * HC;
+  const int h = threadIdx.x >> 4;
+  const int col = kMergeCols * blockIdx.y + 4 * (threadIdx.x & 15);
+  uint16_t* o = a.out + ((size_t)b * a.n_heads + hc * gc + h) * kDc + col;
+  const int u = s_prefix[b + 1] - s_prefix[b];
+  if (u == 0) {  // empty or out-of-range sequence: zeros
+    if (h < gc) *reinterpret_cast<uint2*>(o) = make_uint2(0u, 0u);
+    return;
+  }
+  const long long R = (long long)s_prefix[B] * HC;
+  const int W = effective_wg(a.n_wg, R, s_umax);
+  const int n = u - kSegRowsMla;
+  const long long real0 = (long long)s_prefix[b] * HC + (long long)hc * u + kSegRowsMla;
+  const int w0 = wg_of(real0, R, W);
+  const int np = wg_of(real0 + n - 1, R, W) - w0 + 1;
+  const long long slot0 = (long long)w0 + seg;
+  for (int t = threadIdx.x; t < np * gc; t += kThreads) {
+    const int p = t / gc, hh = t - p * gc;
+    s_w[t] = a.ml[((slot0 + p) * kSlotHeads + hh) * 2];
+    s_l[t] = a.ml[((slot0 + p) * kSlotHeads + hh) * 2 + 1];
+  }
+  __syncthreads();
+  if (threadIdx.x < gc) {  // weights of the normalised partials: 2^(m_p - m*) l_p / l*
+    const int hh = threadIdx.x;
+    float mx = -INFINITY;
+    for (int p = 0; p < np; ++p) mx = fmaxf(mx, s_w[p * gc + hh]);
+    float lsum = 0.0f;
+    for (int p = 0; p < np; ++p) {
+      const float f = __builtin_amdgcn_exp2f(s_w[p * gc + hh] - mx) * s_l[p * gc + hh];
+      s_w[p * gc + hh] = f;
+      lsum += f;
+    }
+    const float inv = 1.0f / lsum;
+    for (int p = 0; p < np; ++p) s_w[p * gc + hh] *= inv;
+  }
+  __syncthreads();
+  if (h >= gc) return;
+  float x[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  constexpr int K = 8;  // pieces per batch of loads
+  for (int p0 = 0; p0 < np; p0 += K) {
+    uint2 v[K];
+#pragma unroll
+    for (int i = 0; i < K; ++i)
+      v[i] = *reinterpret_cast<const uint2*>(a.part + ((slot0 + min(p0 + i, np - 1)) * kSlotHeads + h) * kDc + col);
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      if (p0 + i < np) {
+        const float wt = s_w[(p0 + i) * gc + h];
+        x[0] = fmaf(__uint_as_float(v[i].x << 16), wt, x[0]);
+        x[1] = fmaf(__uint_as_float(v[i].x & 0xFFFF0000u), wt, x[1]);
+        x[2] = fmaf(__uint_as_float(v[i].y << 16), wt, x[2]);
+        x[3] = fmaf(__uint_as_float(v[i].y & 0xFFFF0000u), wt, x[3]);
+      }
+    }
+  }
+  *reinterpret_cast<uint2*>(o) = make_uint2((uint32_t)bf16_rne(x[0]) | ((uint32_t)bf16_rne(x[1]) << 16),
+                                            (uint32_t)bf16_rne(x[2]) | ((uint32_t)bf16_rne(x[3]) << 16));
+}
+
+// ---- absorb and up-projection ---------------------------------------------
+constexpr int kBG = 4;  // sequences per workgroup
+
+// q~[b,h,0:512] = W_UK[h]^T q_nope[b,h] (fp32 sums, rounded to bf16),
+// q~[b,h,512:576] = q_rope[b,h]. grid (H, ceil(B / kBG)), 256 threads; thread
+// t owns latent columns 2t, 2t + 1 for kBG sequences.
+__global__ __launch_bounds__(256) void mla_absorb_kernel(const uint16_t* __restrict__ q_nope,
+                                                         const uint16_t* __restrict__ q_rope,
+                                                         const uint16_t* __restrict__ w_uk,
+                                                         uint16_t* __restrict__ q_abs, int batch, int n_heads,
+                                                         int d_n) {
+  __shared__ float qn[kBG][256];
+  const int h = blockIdx.x;
+  const int b0 = blockIdx.y * kBG;
+  const int t = threadIdx.x;
+  for (int i = t; i < kBG * d_n; i += 256) {
+    const int bb = i / d_n, k = i - bb * d_n;
+    qn[bb][k] = (b0 + bb < batch) ? bf16_to_f32(q_nope[((size_t)(b0 + bb) * n_heads + h) * d_n + k]) : 0.0f;
+  }
+  __syncthreads();
+  float acc[kBG][2];
+#pragma unroll
+  for (int bb = 0; bb < kBG; ++bb) acc[bb][0] = acc[bb][1] = 0.0f;
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(w_uk + (size_t)h * d_n * kDc) + t;
+  for (int k = 0; k < d_n; ++k) {
+    const uint32_t w2 = w[(size_t)k * (kDc / 2)];
+    const float w0 = __uint_as_float(w2 << 16), w1 = __uint_as_float(w2 & 0xFFFF0000u);
+#pragma unroll
+    for (int bb = 0; bb < kBG; ++bb) {
+      acc[bb][0] = fmaf(qn[bb][k], w0, acc[bb][0]);
+      acc[bb][1] = fmaf(qn[bb][k], w1, acc[bb][1]);
+    }
+  }
+#pragma unroll
+  for (int bb = 0; bb < kBG; ++bb) {
+    if (b0 + bb >= batch) break;
+    uint16_t* dst = q_abs + ((size_t)(b0 + bb) * n_heads + h) * kRow;
+    reinterpret_cast<uint32_t*>(dst)[t] = (uint32_t)bf16_rne(acc[bb][0]) | ((uint32_t)bf16_rne(acc[bb][1]) << 16);
+    if (t < kDr) dst[kDc + t] = q_rope[((size_t)(b0 + bb) * n_heads + h) * kDr + t];
+  }
+}
+
+// out[b,h,:] = W_UV[h]^T o~[b,h] (fp32 sums, rounded to bf16). grid (H,
+// ceil(B / kBG)), 256 threads = 4 groups of 128 latent columns x 64 threads
+// of 2 output columns; the groups are summed through LDS.
+__global__ __launch_bounds__(256) void mla_uproj_kernel(const uint16_t* __restrict__ o_lat,
+                                                        const uint16_t* __restrict__ w_uv,
+                                                        uint16_t* __restrict__ out, int batch, int n_heads,
+                                                        int d_v) {
+  __shared__ float ol[kBG][kDc];
+  __shared__ float red[4][kBG][128];
+  const int h = blockIdx.x;
+  const int b0 = blockIdx.y * kBG;
+  const int t = threadIdx.x;
+  for (int i = t; i < kBG * kDc; i += 256) {
+    const int bb = i / kDc, c = i - bb * kDc;
+    ol[bb][c] = (b0 + bb < batch) ? bf16_to_f32(o_lat[((size_t)(b0 + bb) * n_heads + h) * kDc + c]) : 0.0f;
+  }
+  __syncthreads();
+  const int grp = t >> 6;       // latent columns [128 grp, 128 grp + 128)
+  const int pr = t & 63;        // output columns 2 pr, 2 pr + 1
+  float acc[kBG][2];
+#pragma unroll
+  for (int bb = 0; bb < kBG; ++bb) acc[bb][0] = acc[bb][1] = 0.0f;
+  if (2 * pr < d_v) {
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(w_uv + (size_t)h * kDc * d_v) + pr;
+    for (int c = 128 * grp; c < 128 * grp + 128; ++c) {
+      const uint32_t w2 = w[(size_t)c * (d_v / 2)];
+      const float w0 = __uint_as_float(w2 << 16), w1 = __uint_as_float(w2 & 0xFFFF0000u);
+#pragma unroll
+      for (int bb = 0; bb < kBG; ++bb) {
+        acc[bb][0] = fmaf(ol[bb][c], w0, acc[bb][0]);
+        acc[bb][1] = fmaf(ol[bb][c], w1, acc[bb][1]);
+      }
+    }
+  }
+#pragma unroll
+  for (int bb = 0; bb < kBG; ++bb) {
+    red[grp][bb][2 * pr] = acc[bb][0];
+    red[grp][bb][2 * pr + 1] = acc[bb][1];
+  }
+  __syncthreads();
+  for (int i = t; i < kBG * d_v; i += 256) {
+    const int bb = i / d_v, col = i - bb * d_v;
+    if (b0 + bb >= batch) continue;
+    const float x = (red[0][bb][col] + red[1][bb][col]) + (red[2][bb][col] + red[3][bb][col]);
+    out[((size_t)(b0 + bb) * n_heads + h) * d_v + col] = bf16_rne(x);
+  }
+}
+
+}  // namespace
+
+hipError_t kvc_launch_mla_attn(const kvc_cache* c, const void* rows_layer, const void* q_abs, void* out_lat,
+                               const int32_t* valid_lens, const int32_t* cache_index, float sm_scale,
+                               hipStream_t stream) {
+  static int resident = 0;  // workgroups per CU the split kernel keeps resident
+  if (resident == 0) {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, mla_split_kernel, kThreads, 0) != hipSuccess || nb < 1)
+      nb = 1;
+    resident = nb;
+  }
+  MlaArgs a;
+  a.rows = static_cast<const uint16_t*>(rows_layer);
+  a.q_abs = static_cast<const uint16_t*>(q_abs);
+  a.part = reinterpret_cast<uint16_t*>(c->ws_acc);
+  a.ml = c->ws_ml;
+  a.out = static_cast<uint16_t*>(out_lat);
+  a.valid_lens = valid_lens;
+  a.cache_index = cache_index;
+  a.scale_log2 = sm_scale * kLog2e;
+  a.batch = c->d.batch;
+  a.n_heads = c->d.n_heads;
+  a.max_context = c->d.max_context;
+  a.chunk_heads = c->d.n_heads <= kSlotHeads ? c->d.n_heads : kSlotHeads;
+  a.head_chunks = c->d.n_heads / a.chunk_heads;
+  a.n_wg = c->workgroups_forced > 0 ? c->workgroups_forced : resident * c->num_cus;
+  if (a.n_wg > c->max_workgroups) a.n_wg = c->max_workgroups;
+  a.err_flag = c->err_flag;
+  mla_split_kernel<<<dim3(a.n_wg), dim3(kThreads), 0, stream>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  mla_merge_kernel<<<dim3(a.batch * a.head_chunks, kDc / kMergeCols), dim3(kThreads), 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t kvc_launch_mla_absorb(const kvc_cache* c, const void* q_nope, const void* q_rope, const void* w_uk,
+                                 uint16_t* q_abs, hipStream_t stream) {
+  const int B = c->d.batch, H = c->d.n_heads;
+  mla_absorb_kernel<<<dim3(H, (B + kBG - 1) / kBG), dim3(256), 0, stream>>>(
+      static_cast<const uint16_t*>(q_nope), static_cast<const uint16_t*>(q_rope),
+      static_cast<const uint16_t*>(w_uk), q_abs, B, H, c->d.head_dim);
+  return hipGetLastError();
+}
+
+hipError_t kvc_launch_mla_uproj(const kvc_cache* c, const uint16_t* o_lat, const void* w_uv, void* out,
+                                hipStream_t stream) {
+  const int B = c->d.batch, H = c->d.n_heads;
+  mla_uproj_kernel<<<dim3(H, (B + kBG - 1) / kBG), dim3(256), 0, stream>>>(
+      o_lat, static_cast<const uint16_t*>(w_uv), static_cast<uint16_t*>(out), B, H, c->d.head_dim);
+  return hipGetLastError();
 }

@@ -90,6 +90,17 @@ def test_unsupported_head_dim_and_null(lib):
     assert lib.kvc_bytes(ctypes.byref(kvc.gqa_desc(1, 1, 4, 4, 32, 16, "bf16")), None) == kvc.KVC_ERR_INVALID_ARG
 
 
+@pytest.mark.parametrize("desc", [
+    kvc.mla_desc(1, 2, 24, 64),                 # latent heads: <= 16 or a multiple of 16
+    kvc.mla_desc(1, 1, 16, 1 << 20),            # latent rows of one sequence >= 2^30 bytes
+    kvc.gqa_desc(1, 1, 8, 8, 256, 1 << 21, "bf16"),   # one (sequence, kv head) block >= 2^30 bytes
+    kvc.gqa_desc(1, 2048, 8, 8, 32, 1 << 20, "bf16"),  # row space of all sequences >= 2^31
+], ids=["mla_heads", "mla_rows", "gqa_block", "row_space"])
+def test_unsupported_sizes(lib, desc):
+    out = ctypes.c_uint64(0)
+    assert lib.kvc_bytes(ctypes.byref(desc), ctypes.byref(out)) == kvc.KVC_ERR_UNSUPPORTED
+
+
 def test_host_only_calls_reject_null_handles(lib):
     k, v = ctypes.c_void_p(), ctypes.c_void_p()
     assert lib.kvc_layer_ptrs(None, 0, ctypes.byref(k), ctypes.byref(v)) == kvc.KVC_ERR_INVALID_ARG
