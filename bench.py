@@ -51,6 +51,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-repeats", type=int, default=100)
     p.add_argument("--eager-only", action="store_true", help="skip the graph-replay leg")
+    p.add_argument("--no-mla", action="store_true", help="skip the latent (MLA) leg")
     p.add_argument("--workgroups", type=int, default=0,
                    help="force the persistent attention grid size (0 = device default)")
     return p.parse_args()
@@ -132,6 +133,94 @@ class Workload:
     def step(self):
         for layer in range(self.L):
             self.layer_step(layer)
+
+
+class MlaWorkload:
+    """The latent (MLA) workload: B=32, H=16, 576-wide rows (latent 512 +
+    rotary key 64), 4096 valid rows per sequence, bf16. One layer is 151 MB,
+    under the 256 MB Infinity Cache, so 8 layer copies (1.2 GB) are rotated
+    to make the reads come from HBM; each layer has its own weights."""
+
+    N_LAYERS = 8
+
+    def __init__(self, torch, dev):
+        from static_kv_cache_amd import kvc, synthetic
+        self.torch, self.kvc = torch, kvc
+        cfg = synthetic.WORKLOADS["mla_latent_bf16"]
+        self.cfg = cfg
+        B, H, S = cfg["batch"], cfg["n_heads"], cfg["max_context"]
+        self.B, self.H, self.S, self.L = B, H, S, self.N_LAYERS
+        self.cache = kvc.Cache(kvc.mla_desc(self.L, B, H, S))
+        d = synthetic.mla_layer(cfg)
+        rows = kvc.to_device(d["rows_fill"], dev)
+        for layer in range(self.L):
+            self.cache.prefill_fill(layer, rows, None, 0)
+        del rows
+        rng = np.random.default_rng(cfg["seed"] + 7)
+        dn, dc, dr = cfg["nope_dim"], cfg["latent_dim"], cfg["rope_dim"]
+        self.rows_new = kvc.to_device(d["rows_new"], dev)
+        self.q_nope = kvc.to_device(d["q_nope"], dev)
+        self.q_rope = kvc.to_device(d["q_rope"], dev)
+        self.w_uk = [kvc.to_device(synthetic.draw(rng, (H, dn, dc), "bf16", std=cfg["w_std"]), dev)
+                     for _ in range(self.L)]
+        self.w_uv = [kvc.to_device(synthetic.draw(rng, (H, dc, dn), "bf16", std=cfg["w_std"]), dev)
+                     for _ in range(self.L)]
+        q_abs = rng.standard_normal((B, H, dc + dr)).astype(np.float32)
+        q_abs[..., :dc] *= np.float32(np.sqrt(dn) * cfg["w_std"])
+        self.q_abs = kvc.to_device(synthetic.f32_to_bf16_bits(q_abs), dev)
+        self.o_lat = torch.empty((B, H, dc), dtype=torch.bfloat16, device=dev)
+        self.out = torch.empty((B, H, dn), dtype=torch.bfloat16, device=dev)
+        self.valid = kvc.to_device(d["valid_lens"], dev)
+        self.ci = kvc.to_device(d["cache_index"], dev)
+        self.sm_scale = d["sm_scale"]
+        self.kv_bytes = int(d["valid_lens"].sum()) * (dc + dr) * 2
+        torch.cuda.synchronize()
+        self.cache.check()
+
+    def latent(self, layer):
+        self.cache.decode_attn(layer, self.q_abs, self.o_lat, valid_lens=self.valid, sm_scale=self.sm_scale)
+
+    def layer_step(self, layer):
+        self.cache.append(layer, self.rows_new, None, self.ci)
+        self.cache.mla_decode(layer, self.q_nope, self.q_rope, self.w_uk[layer], self.w_uv[layer], self.out,
+                              valid_lens=self.valid, sm_scale=self.sm_scale)
+
+
+def bench_mla(torch, steps, warmup):
+    """Latent attention alone (kvc_decode_attn on the latent cache: split +
+    merge kernels) and the whole latent step (append + kvc_mla_decode:
+    absorb, split, merge, up-projection), per layer, from HIP events around
+    bursts of back-to-back launches over the rotated layers."""
+    wl = MlaWorkload(torch, torch.device("cuda:0"))
+    L = wl.L
+
+    def burst(fn):
+        for _ in range(warmup):
+            for layer in range(L):
+                fn(layer)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        torch.cuda.synchronize()
+        for e0, e1 in evs:
+            e0.record()
+            for layer in range(L):
+                fn(layer)
+            e1.record()
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) / L for a, b in evs]))
+
+    lat_ms = burst(wl.latent)
+    step_ms = burst(wl.layer_step)
+    wl.cache.check()
+    gbs = wl.kv_bytes / (lat_ms * 1e-3) / 1e9
+    res = dict(workload="mla_latent_bf16", batch=wl.B, n_heads=wl.H, latent_dim=512, rope_dim=64,
+               max_context=wl.S, valid_len=wl.S, layer_copies=L, kv_bytes_per_layer=wl.kv_bytes,
+               latent_attn_us=round(lat_ms * 1e3, 3), kv_gbs=round(gbs, 2),
+               hbm_peak_frac=round(gbs / HBM_PEAK_GBS, 4),
+               step_us=round(step_ms * 1e3, 3), layer_steps_per_s=round(1.0 / (step_ms * 1e-3), 1),
+               step="append + absorb + latent attention (split, merge) + up-projection")
+    log(f"bench: mla latent attention {lat_ms * 1e3:.2f} us ({gbs:.1f} GB/s), step {step_ms * 1e3:.2f} us")
+    wl.cache.free()
+    return res
 
 
 def time_steps(torch, fn, steps):
@@ -257,6 +346,9 @@ def main():
                 alg_bytes_per_launch=wl.decode_alg_bytes, mean_launch_us=round(decode_ms * 1e3, 3),
                 timing=f"HIP events on the launch stream, {args.steps} bursts of {L} back-to-back launches",
                 event_pair_us=round(pair_ms * 1e3, 3))
+    wg_forced = wl.cache.workgroups()[0]
+    wl.cache.free()
+    mla = None if args.no_mla else bench_mla(torch, max(5, args.steps // 2), 2)
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl, args.cpu_repeats)
     line = {
         "metric": METRIC,
@@ -278,14 +370,14 @@ def main():
         "config": {"workload": WORKLOAD, "n_layers": L, "batch": wl.B, "n_heads": wl.H,
                    "n_kv_heads": wl.Hkv, "head_dim": wl.D, "max_context": wl.S,
                    "valid_len": "U[1024,4096] seed 2", "sum_valid_len": wl.sum_valid,
-                   "workgroups": wl.cache.workgroups()[0] or "resident",
+                   "workgroups": wg_forced or "resident",
                    "launch": "hipgraph" if ms_graph is not None else "eager",
                    "step": "32 x (append + decode attention)"},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "mla": mla,
     }
     print(json.dumps(line), flush=True)
-    wl.cache.free()
 
 
 if __name__ == "__main__":

@@ -488,6 +488,11 @@ struct MfmaPiece {
 
   static __device__ __forceinline__ void run(const DecodeArgs& a, Smem& sm, int b, int kvg, int chunk,
                                              int r_begin, int r_end, bool whole, long long slot) {
+    b = uniform(b);
+    kvg = uniform(kvg);
+    chunk = uniform(chunk);
+    r_begin = uniform(r_begin);
+    r_end = uniform(r_end);
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int g = lane >> 4;
@@ -524,9 +529,8 @@ struct MfmaPiece {
     // (sequence, kv head): loads of rows past the end (the tail of the last
     // tile, prefetches past the piece) return zeros without touching memory,
     // and their scores are masked below.
-    const int nbytes = r_end * (2 * D);
-    const __amdgpu_buffer_rsrc_t kres = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, 0, nbytes, kBufWord3);
-    const __amdgpu_buffer_rsrc_t vres = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, 0, nbytes, kBufWord3);
+    const __amdgpu_buffer_rsrc_t kres = buffer_rsrc(kbase, r_end * (2 * D));
+    const __amdgpu_buffer_rsrc_t vres = buffer_rsrc(vbase, r_end * (2 * D));
     const int koff = j * (2 * D) + 16 * g;  // K row base + j, dims 8g.. of each 32-dim step
     const int voff = lane * 16;             // V tile as contiguous 16-byte chunks
 

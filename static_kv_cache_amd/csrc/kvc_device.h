@@ -20,6 +20,24 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
+// Values the caller knows to be the same in every lane (derived from shared
+// memory or kernel arguments), taken from the first lane so the compiler
+// keeps them in scalar registers: loop bounds become scalar branches, and a
+// buffer descriptor built from them stays in SGPRs (a descriptor the
+// compiler thinks divergent wraps every load in a waterfall loop).
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ const void* uniform(const void* p) {
+  const uint64_t a = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return (const void*)(((uint64_t)hi << 32) | lo);
+}
+// Raw buffer descriptor over [p, p + nbytes) (p and nbytes wave-uniform):
+// loads at or past nbytes return zeros without touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, int nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(uniform(p)), 0, uniform(nbytes), kBufWord3);
+}
+
 // fp32 -> bf16 bits, round to nearest, ties to even; NaN stays a quiet NaN.
 __device__ __forceinline__ uint16_t bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);

@@ -17,13 +17,14 @@
 //    on the matrix cores. Work space as for GQA (row space of segments =
 //    (sequence, chunk of up to 16 heads), persistent grid, pieces). A
 //    workgroup streams its rows in tiles of 32 rows (36 KB, one contiguous
-//    block) staged through a skewed LDS tile; the next tile is in flight in
-//    registers while the current one is used. The latent rows are read from
+//    block) staged through a skewed LDS tile; the next two tiles are in
+//    flight in registers while the current one is used. The latent rows are read from
 //    HBM once for all heads of the chunk.
-//  - Every wave computes the whole score tile S = R_tile q~^T
-//    (v_mfma_f32_16x16x32_bf16, 18 steps of 32 dims, rows as the A operand
-//    read from LDS, the heads as the B operand held in registers), so every
-//    wave holds identical softmax state and no exchange is needed; then
+//  - The score tile S = R_tile q~^T is split over the 576 dims: each wave
+//    takes a quarter (144 dims, v_mfma_f32_16x16x16_bf16 with the rows as
+//    the A operand read from LDS and the heads as the B operand held in
+//    registers); the four partial tiles are summed through LDS in the same
+//    order by every wave, so all waves hold identical softmax state. Then
 //    each wave applies P to its own quarter (128) of the 512 latent columns
 //    (v_mfma_f32_16x16x16_bf16 with the rows reaching the B operand through
 //    ds_read_b64_tr_b16).
@@ -32,7 +33,8 @@
 //    with weights 2^(m_p - m*) l_p / l*. A latent partial is 16 x 512 wide,
 //    too wide for one workgroup to merge at the end of the streaming kernel.
 //  - The absorb and up-projection are small batched products over the
-//    weights (2 MB each), done with fp32 FMAs on the vector units.
+//    weights (2 MB each), on the matrix cores with the weight block staged
+//    in LDS.
 
 #include "kvc_device.h"
 
@@ -50,7 +52,8 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kCols = kDc / kWaves;          // latent columns per wave in p.v (128)
 constexpr int kNB = kCols / 16;              // output column blocks per wave
-constexpr int kKS = kRow / 32;               // q.k steps of 32 dims
+constexpr int kQDims = kRow / kWaves;        // q.k dims per wave (144)
+constexpr int kQS = kQDims / 16;             // q.k steps of 16 dims per wave
 constexpr int kVec = kTok * kRowBytes / 16 / kThreads;  // staged 16-byte vectors per thread per tile
 constexpr int kRowVecs = kRowBytes / 16;     // 72
 constexpr int kSlotHeads = 16;               // partial entries per workspace slot
@@ -75,8 +78,13 @@ struct MlaArgs {
 };
 
 // Rows [r_begin, r_end) of sequence b against heads [hc * gc, (hc + 1) * gc).
-__device__ __forceinline__ void mla_piece(const MlaArgs& a, unsigned char* tile, int b, int hc, int r_begin,
-                                          int r_end, long long slot) {
+// sred: 8 KB of LDS for the per-wave partial score tiles.
+__device__ __forceinline__ void mla_piece(const MlaArgs& a, unsigned char* tile, f32x4_t* sred, int b, int hc,
+                                          int r_begin, int r_end, long long slot) {
+  b = uniform(b);
+  hc = uniform(hc);
+  r_begin = uniform(r_begin);
+  r_end = uniform(r_end);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int g = lane >> 4;
@@ -85,15 +93,15 @@ __device__ __forceinline__ void mla_piece(const MlaArgs& a, unsigned char* tile,
   const int h0 = hc * gc;
   const float scale_log2 = a.scale_log2;
 
-  // q~ as the B operand: column j is head h0 + j, zero past the chunk
-  bf16x8_t qb[kKS];
+  // q~ as the B operand of this wave's quarter of the 576 dims (k steps of
+  // 16): column j is head h0 + j, zero past the chunk
+  s16x4_t qb[kQS];
   const bool real = j < gc;
-  const uint16_t* qh = a.q_abs + ((size_t)b * a.n_heads + h0 + (real ? j : 0)) * kRow;
+  const uint16_t* qh = a.q_abs + ((size_t)b * a.n_heads + h0 + (real ? j : 0)) * kRow + kQDims * wave + 4 * g;
 #pragma unroll
-  for (int k = 0; k < kKS; ++k) {
-    u32x4_t v = *reinterpret_cast<const u32x4_t*>(qh + 32 * k + 8 * g);
-    v = real ? v : u32x4_t{0u, 0u, 0u, 0u};
-    qb[k] = __builtin_bit_cast(bf16x8_t, v);
+  for (int k = 0; k < kQS; ++k) {
+    s16x4_t v = *reinterpret_cast<const s16x4_t*>(qh + 16 * k);
+    qb[k] = real ? v : s16x4_t{0, 0, 0, 0};
   }
 
   f32x4_t o[kNB];
@@ -103,42 +111,47 @@ __device__ __forceinline__ void mla_piece(const MlaArgs& a, unsigned char* tile,
   float l = 0.0f;       // this lane's share of column j's denominator
 
   // The resource spans exactly rows [0, r_end) of the sequence: loads past
-  // the end (the tail of the last tile, the prefetch after it) return zeros
+  // the end (the tail of the last tile, prefetches after it) return zeros
   // without touching memory, and their scores are masked.
   const uint16_t* seq = a.rows + (size_t)b * a.max_context * kRow;
-  const __amdgpu_buffer_rsrc_t res = __builtin_amdgcn_make_buffer_rsrc((void*)seq, 0, r_end * kRowBytes, kBufWord3);
-  u32x4_t st[kVec];
-  auto load = [&](int t0) {
+  const __amdgpu_buffer_rsrc_t res = buffer_rsrc(seq, r_end * kRowBytes);
+  auto load = [&](u32x4_t (&st)[kVec], int t0) {
     const int off = t0 * kRowBytes + (int)threadIdx.x * 16;
 #pragma unroll
     for (int i = 0; i < kVec; ++i) st[i] = __builtin_amdgcn_raw_buffer_load_b128(res, off + i * 16 * kThreads, 0, 0);
   };
-  auto stage = [&]() {
+  auto stage = [&](const u32x4_t (&st)[kVec]) {
 #pragma unroll
     for (int i = 0; i < kVec; ++i) {
       const int f = (int)threadIdx.x + i * kThreads;
       *reinterpret_cast<u32x4_t*>(tile + (f / kRowVecs) * kStride + (f % kRowVecs) * 16) = st[i];
     }
   };
-
-  load(r_begin);
-  for (int t0 = r_begin; t0 < r_end; t0 += kTok) {
-    __syncthreads();  // every wave is done with the previous tile
-    stage();
-    load(t0 + kTok);  // next tile in flight while this one is used
-    __syncthreads();  // the tile is visible
-
-    // scores of two 16-row blocks: s[tb][t] = R[t0 + 16 tb + 4g + t] . q~[head j]
+  // One tile whose rows start at t0 (rows at or past r_end are masked; a
+  // tile wholly past the end changes nothing).
+  auto use_tile = [&](int t0) {
+    // this wave's partial scores over its 144 dims, two 16-row blocks
+    f32x4_t sp[2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      sp[tb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      const unsigned char* arow = tile + (16 * tb + j) * kStride + 2 * kQDims * wave + 8 * g;
+#pragma unroll
+      for (int k = 0; k < kQS; ++k) {
+        const s16x4_t av = *reinterpret_cast<const s16x4_t*>(arow + 32 * k);
+        sp[tb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, qb[k], sp[tb], 0, 0, 0);
+      }
+      sred[(wave * 2 + tb) * 64 + lane] = sp[tb];
+    }
+    __syncthreads();  // partial scores visible
+    // full scores, summed in the same order by every wave (identical softmax
+    // state in all waves): s[tb][t] = R[t0 + 16 tb + 4g + t] . q~[head j]
     f32x4_t s[2];
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
-      s[tb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-      const unsigned char* arow = tile + (16 * tb + j) * kStride + 16 * g;
+      s[tb] = sred[tb * 64 + lane];
 #pragma unroll
-      for (int k = 0; k < kKS; ++k) {
-        const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(arow + 64 * k);
-        s[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qb[k], s[tb], 0, 0, 0);
-      }
+      for (int w = 1; w < kWaves; ++w) s[tb] += sred[(w * 2 + tb) * 64 + lane];
     }
     if (t0 + kTok > r_end) {
 #pragma unroll
@@ -147,8 +160,8 @@ __device__ __forceinline__ void mla_piece(const MlaArgs& a, unsigned char* tile,
         for (int t = 0; t < 4; ++t) s[tb][t] = (t0 + 16 * tb + 4 * g + t < r_end) ? s[tb][t] : -INFINITY;
     }
     // online softmax with a lazily moved reference maximum (p <= 2^kLazyMfma)
-    float cand = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                       fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3]))) * scale_log2;
+    const float cand = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                             fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3]))) * scale_log2;
     if (__builtin_amdgcn_ballot_w64(cand > m + kLazyMfma)) {
       float mt = fmaxf(cand, __shfl_xor(cand, 16));
       mt = fmaxf(mt, __shfl_xor(mt, 32));
@@ -184,6 +197,24 @@ __device__ __forceinline__ void mla_piece(const MlaArgs& a, unsigned char* tile,
         o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa[tb], vb, o[nb], 0, 0, 0);
       }
     }
+  };
+
+  // Two register tiles in flight: the body is straight-line over a pair of
+  // tiles, so the wait before staging one leaves the other's loads pending.
+  u32x4_t st0[kVec], st1[kVec];
+  load(st0, r_begin);
+  load(st1, r_begin + kTok);
+  for (int t0 = r_begin; t0 < r_end; t0 += 2 * kTok) {
+    __syncthreads();  // every wave is done with the previous tile
+    stage(st0);
+    load(st0, t0 + 2 * kTok);
+    __syncthreads();  // the tile is visible
+    use_tile(t0);
+    __syncthreads();
+    stage(st1);
+    load(st1, t0 + 3 * kTok);
+    __syncthreads();
+    use_tile(t0 + kTok);
   }
 
   // denominators of the head columns, then the partial o~ / l, m and l
@@ -210,6 +241,7 @@ __device__ __forceinline__ void mla_piece(const MlaArgs& a, unsigned char* tile,
 // Persistent latent attention: grid = W workgroups of 256 threads.
 __global__ __launch_bounds__(kThreads) void mla_split_kernel(MlaArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char tile[kTok * kStride];
+  __shared__ f32x4_t sred[kWaves * 2 * 64];
   __shared__ int32_t s_prefix[KVC_MAX_BATCH + 1];
   __shared__ int32_t s_umax;
   const int B = a.batch;
@@ -225,7 +257,7 @@ __global__ __launch_bounds__(kThreads) void mla_split_kernel(MlaArgs a) {
   if (x >= hi) return;
   for_each_piece(s_prefix, B, HC, kSegRowsMla, x, hi,
                  [&](int b, int hc, int r_begin, int r_end, int, long long) {
-                   mla_piece(a, tile, b, hc, r_begin, r_end, (long long)w + (long long)b * HC + hc);
+                   mla_piece(a, tile, sred, b, hc, r_begin, r_end, (long long)w + (long long)b * HC + hc);
                  });
 }
 
@@ -236,8 +268,9 @@ constexpr int kMergeCols = 64;
 __global__ __launch_bounds__(kThreads) void mla_merge_kernel(MlaArgs a) {
   __shared__ int32_t s_prefix[KVC_MAX_BATCH + 1];
   __shared__ int32_t s_umax;
-  __shared__ float s_w[kMaxMerge * kSlotHeads];  // m_p, then the weight of piece p (head-minor)
-  __shared__ float s_l[kMaxMerge * kSlotHeads];
+  __shared__ float s_m[kMaxMerge * kSlotHeads];  // m_p of (piece p, head), head-minor
+  __shared__ float s_l[kMaxMerge * kSlotHeads];  // l_p
+  __shared__ float s_w[kMaxMerge * kSlotHeads];  // weight of the normalised partial
   const int B = a.batch;
   build_row_space(a.valid_lens, a.cache_index, B, a.max_context, kSegRowsMla, s_prefix, &s_umax, a.err_flag,
                   false);
@@ -261,34 +294,37 @@ __global__ __launch_bounds__(kThreads) void mla_merge_kernel(MlaArgs a) {
   const int w0 = wg_of(real0, R, W);
   const int np = wg_of(real0 + n - 1, R, W) - w0 + 1;
   const long long slot0 = (long long)w0 + seg;
+  // This thread's partial columns for the first K pieces are requested
+  // before the weights are worked out, so both loads overlap.
+  constexpr int K = 16;
+  const uint16_t* pc = a.part + (slot0 * kSlotHeads + (h < gc ? h : 0)) * kDc + col;
+  uint2 v[K];
+#pragma unroll
+  for (int i = 0; i < K; ++i) v[i] = *reinterpret_cast<const uint2*>(pc + (size_t)min(i, np - 1) * kSlotHeads * kDc);
   for (int t = threadIdx.x; t < np * gc; t += kThreads) {
     const int p = t / gc, hh = t - p * gc;
-    s_w[t] = a.ml[((slot0 + p) * kSlotHeads + hh) * 2];
+    s_m[t] = a.ml[((slot0 + p) * kSlotHeads + hh) * 2];
     s_l[t] = a.ml[((slot0 + p) * kSlotHeads + hh) * 2 + 1];
   }
   __syncthreads();
-  if (threadIdx.x < gc) {  // weights of the normalised partials: 2^(m_p - m*) l_p / l*
-    const int hh = threadIdx.x;
+  // weight of (piece p, head hh), one per thread: 2^(m_p - m*) l_p / l*
+  for (int t = threadIdx.x; t < np * gc; t += kThreads) {
+    const int hh = t % gc;
     float mx = -INFINITY;
-    for (int p = 0; p < np; ++p) mx = fmaxf(mx, s_w[p * gc + hh]);
+    for (int p = 0; p < np; ++p) mx = fmaxf(mx, s_m[p * gc + hh]);
     float lsum = 0.0f;
-    for (int p = 0; p < np; ++p) {
-      const float f = __builtin_amdgcn_exp2f(s_w[p * gc + hh] - mx) * s_l[p * gc + hh];
-      s_w[p * gc + hh] = f;
-      lsum += f;
-    }
-    const float inv = 1.0f / lsum;
-    for (int p = 0; p < np; ++p) s_w[p * gc + hh] *= inv;
+    for (int p = 0; p < np; ++p) lsum += __builtin_amdgcn_exp2f(s_m[p * gc + hh] - mx) * s_l[p * gc + hh];
+    s_w[t] = __builtin_amdgcn_exp2f(s_m[t] - mx) * s_l[t] / lsum;
   }
   __syncthreads();
   if (h >= gc) return;
   float x[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  constexpr int K = 8;  // pieces per batch of loads
   for (int p0 = 0; p0 < np; p0 += K) {
-    uint2 v[K];
+    if (p0 > 0) {
 #pragma unroll
-    for (int i = 0; i < K; ++i)
-      v[i] = *reinterpret_cast<const uint2*>(a.part + ((slot0 + min(p0 + i, np - 1)) * kSlotHeads + h) * kDc + col);
+      for (int i = 0; i < K; ++i)
+        v[i] = *reinterpret_cast<const uint2*>(pc + (size_t)min(p0 + i, np - 1) * kSlotHeads * kDc);
+    }
 #pragma unroll
     for (int i = 0; i < K; ++i) {
       if (p0 + i < np) {
@@ -305,92 +341,77 @@ __global__ __launch_bounds__(kThreads) void mla_merge_kernel(MlaArgs a) {
 }
 
 // ---- absorb and up-projection ---------------------------------------------
-constexpr int kBG = 4;  // sequences per workgroup
+//
+// Both are batched products over the heads with the batch as M:
+//   absorb:  q~[:, h, 0:512] = q_nope[:, h, :] (B x 128)  . W_UK[h] (128 x 512)
+//   up-proj: out[:, h, :]     = o~[:, h, :]    (B x 512)  . W_UV[h] (512 x 128)
+// The weight block W[h][:, n0:n0+64] is staged row-major in LDS (K rows of
+// 128 bytes + skew) and reaches the B operand of v_mfma_f32_16x16x16_bf16
+// through ds_read_b64_tr_b16 (the weights are stored K-major, so this is
+// the transpose the operand needs); the A operand (4 consecutive k of one
+// batch row) is read straight from global memory. Wave w owns output
+// columns n0 + 16 w .. +16; batch rows go 16 at a time. fp32 sums, bf16 out.
+constexpr int kGemmN = 64;                    // output columns per workgroup
+constexpr int kGemmStride = 2 * kGemmN + 16;  // LDS bytes per staged weight row
 
-// q~[b,h,0:512] = W_UK[h]^T q_nope[b,h] (fp32 sums, rounded to bf16),
-// q~[b,h,512:576] = q_rope[b,h]. grid (H, ceil(B / kBG)), 256 threads; thread
-// t owns latent columns 2t, 2t + 1 for kBG sequences.
-__global__ __launch_bounds__(256) void mla_absorb_kernel(const uint16_t* __restrict__ q_nope,
-                                                         const uint16_t* __restrict__ q_rope,
-                                                         const uint16_t* __restrict__ w_uk,
-                                                         uint16_t* __restrict__ q_abs, int batch, int n_heads,
-                                                         int d_n) {
-  __shared__ float qn[kBG][256];
+template <int K>
+__global__ __launch_bounds__(256) void mla_gemm_kernel(const uint16_t* __restrict__ a, long long a_head,
+                                                       long long lda, const uint16_t* __restrict__ w,
+                                                       int n_total, uint16_t* __restrict__ c, long long c_head,
+                                                       long long ldc, int m_total,
+                                                       const uint16_t* __restrict__ rope, int n_heads) {
+  __shared__ __attribute__((aligned(16))) unsigned char wt[K * kGemmStride];
   const int h = blockIdx.x;
-  const int b0 = blockIdx.y * kBG;
-  const int t = threadIdx.x;
-  for (int i = t; i < kBG * d_n; i += 256) {
-    const int bb = i / d_n, k = i - bb * d_n;
-    qn[bb][k] = (b0 + bb < batch) ? bf16_to_f32(q_nope[((size_t)(b0 + bb) * n_heads + h) * d_n + k]) : 0.0f;
+  const int n0 = blockIdx.y * kGemmN;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 4;
+  const int j = lane & 15;
+  // stage W[h][0:K][n0:n0+64] (16-byte vectors, 8 per row): all loads first
+  constexpr int kPer = K * 8 / 256;
+  static_assert(K * 8 % 256 == 0, "weight block must split evenly over the threads");
+  const uint16_t* wh = w + (size_t)h * K * n_total + n0;
+  u32x4_t wv[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int f = (int)threadIdx.x + 256 * i;
+    wv[i] = *reinterpret_cast<const u32x4_t*>(wh + (size_t)(f >> 3) * n_total + 8 * (f & 7));
   }
-  __syncthreads();
-  float acc[kBG][2];
 #pragma unroll
-  for (int bb = 0; bb < kBG; ++bb) acc[bb][0] = acc[bb][1] = 0.0f;
-  const uint32_t* w = reinterpret_cast<const uint32_t*>(w_uk + (size_t)h * d_n * kDc) + t;
-  for (int k = 0; k < d_n; ++k) {
-    const uint32_t w2 = w[(size_t)k * (kDc / 2)];
-    const float w0 = __uint_as_float(w2 << 16), w1 = __uint_as_float(w2 & 0xFFFF0000u);
-#pragma unroll
-    for (int bb = 0; bb < kBG; ++bb) {
-      acc[bb][0] = fmaf(qn[bb][k], w0, acc[bb][0]);
-      acc[bb][1] = fmaf(qn[bb][k], w1, acc[bb][1]);
+  for (int i = 0; i < kPer; ++i) {
+    const int f = (int)threadIdx.x + 256 * i;
+    *reinterpret_cast<u32x4_t*>(wt + (f >> 3) * kGemmStride + 16 * (f & 7)) = wv[i];
+  }
+  // absorb only: the first column block of each head also copies q_rope
+  // into columns [512, 576) of q~
+  if (rope && blockIdx.y == 0) {
+    for (int i = threadIdx.x; i < m_total * kDr; i += 256) {
+      const int b = i / kDr, r = i - b * kDr;
+      c[(size_t)h * c_head + (size_t)b * ldc + kDc + r] = rope[((size_t)b * n_heads + h) * kDr + r];
     }
   }
-#pragma unroll
-  for (int bb = 0; bb < kBG; ++bb) {
-    if (b0 + bb >= batch) break;
-    uint16_t* dst = q_abs + ((size_t)(b0 + bb) * n_heads + h) * kRow;
-    reinterpret_cast<uint32_t*>(dst)[t] = (uint32_t)bf16_rne(acc[bb][0]) | ((uint32_t)bf16_rne(acc[bb][1]) << 16);
-    if (t < kDr) dst[kDc + t] = q_rope[((size_t)(b0 + bb) * n_heads + h) * kDr + t];
-  }
-}
-
-// out[b,h,:] = W_UV[h]^T o~[b,h] (fp32 sums, rounded to bf16). grid (H,
-// ceil(B / kBG)), 256 threads = 4 groups of 128 latent columns x 64 threads
-// of 2 output columns; the groups are summed through LDS.
-__global__ __launch_bounds__(256) void mla_uproj_kernel(const uint16_t* __restrict__ o_lat,
-                                                        const uint16_t* __restrict__ w_uv,
-                                                        uint16_t* __restrict__ out, int batch, int n_heads,
-                                                        int d_v) {
-  __shared__ float ol[kBG][kDc];
-  __shared__ float red[4][kBG][128];
-  const int h = blockIdx.x;
-  const int b0 = blockIdx.y * kBG;
-  const int t = threadIdx.x;
-  for (int i = t; i < kBG * kDc; i += 256) {
-    const int bb = i / kDc, c = i - bb * kDc;
-    ol[bb][c] = (b0 + bb < batch) ? bf16_to_f32(o_lat[((size_t)(b0 + bb) * n_heads + h) * kDc + c]) : 0.0f;
-  }
   __syncthreads();
-  const int grp = t >> 6;       // latent columns [128 grp, 128 grp + 128)
-  const int pr = t & 63;        // output columns 2 pr, 2 pr + 1
-  float acc[kBG][2];
+  const uint16_t* ah = a + (size_t)h * a_head;
+  uint16_t* ch = c + (size_t)h * c_head + n0 + 16 * wave + j;
+  // B operand rows 4g + t of each 16-row k step, columns 16 wave + i, read transposed
+  const unsigned char* brow = wt + (4 * g + (j >> 2)) * kGemmStride + 32 * wave + 8 * (j & 3);
+  for (int m0 = 0; m0 < m_total; m0 += 16) {
+    const int mr = min(m0 + j, m_total - 1);  // A row of this lane (clamped; rows past the end are not stored)
+    const uint16_t* arow = ah + (size_t)mr * lda + 4 * g;
+    f32x4_t acc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int bb = 0; bb < kBG; ++bb) acc[bb][0] = acc[bb][1] = 0.0f;
-  if (2 * pr < d_v) {
-    const uint32_t* w = reinterpret_cast<const uint32_t*>(w_uv + (size_t)h * kDc * d_v) + pr;
-    for (int c = 128 * grp; c < 128 * grp + 128; ++c) {
-      const uint32_t w2 = w[(size_t)c * (d_v / 2)];
-      const float w0 = __uint_as_float(w2 << 16), w1 = __uint_as_float(w2 & 0xFFFF0000u);
-#pragma unroll
-      for (int bb = 0; bb < kBG; ++bb) {
-        acc[bb][0] = fmaf(ol[bb][c], w0, acc[bb][0]);
-        acc[bb][1] = fmaf(ol[bb][c], w1, acc[bb][1]);
-      }
+    for (int k0 = 0; k0 < K; k0 += 16) {
+      const s16x4_t av = *reinterpret_cast<const s16x4_t*>(arow + k0);
+      const s16x4_t bv = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4_t*)(brow + k0 * kGemmStride));
+      acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, acc, 0, 0, 0);
     }
-  }
+    // D row 4g + t is batch row m0 + 4g + t, column j
 #pragma unroll
-  for (int bb = 0; bb < kBG; ++bb) {
-    red[grp][bb][2 * pr] = acc[bb][0];
-    red[grp][bb][2 * pr + 1] = acc[bb][1];
-  }
-  __syncthreads();
-  for (int i = t; i < kBG * d_v; i += 256) {
-    const int bb = i / d_v, col = i - bb * d_v;
-    if (b0 + bb >= batch) continue;
-    const float x = (red[0][bb][col] + red[1][bb][col]) + (red[2][bb][col] + red[3][bb][col]);
-    out[((size_t)(b0 + bb) * n_heads + h) * d_v + col] = bf16_rne(x);
+    for (int t = 0; t < 4; ++t) {
+      const int m = m0 + 4 * g + t;
+      if (m < m_total) ch[(size_t)m * ldc] = bf16_rne(acc[t]);
+    }
   }
 }
 
@@ -432,17 +453,20 @@ hipError_t kvc_launch_mla_attn(const kvc_cache* c, const void* rows_layer, const
 
 hipError_t kvc_launch_mla_absorb(const kvc_cache* c, const void* q_nope, const void* q_rope, const void* w_uk,
                                  uint16_t* q_abs, hipStream_t stream) {
-  const int B = c->d.batch, H = c->d.n_heads;
-  mla_absorb_kernel<<<dim3(H, (B + kBG - 1) / kBG), dim3(256), 0, stream>>>(
-      static_cast<const uint16_t*>(q_nope), static_cast<const uint16_t*>(q_rope),
-      static_cast<const uint16_t*>(w_uk), q_abs, B, H, c->d.head_dim);
+  const int B = c->d.batch, H = c->d.n_heads, dn = c->d.head_dim;
+  if (dn != 128) return hipErrorInvalidValue;
+  mla_gemm_kernel<128><<<dim3(H, kDc / kGemmN), dim3(256), 0, stream>>>(
+      static_cast<const uint16_t*>(q_nope), dn, (long long)H * dn, static_cast<const uint16_t*>(w_uk), kDc, q_abs,
+      kRow, (long long)H * kRow, B, static_cast<const uint16_t*>(q_rope), H);
   return hipGetLastError();
 }
 
 hipError_t kvc_launch_mla_uproj(const kvc_cache* c, const uint16_t* o_lat, const void* w_uv, void* out,
                                 hipStream_t stream) {
-  const int B = c->d.batch, H = c->d.n_heads;
-  mla_uproj_kernel<<<dim3(H, (B + kBG - 1) / kBG), dim3(256), 0, stream>>>(
-      o_lat, static_cast<const uint16_t*>(w_uv), static_cast<uint16_t*>(out), B, H, c->d.head_dim);
+  const int B = c->d.batch, H = c->d.n_heads, dv = c->d.head_dim;
+  if (dv != 128) return hipErrorInvalidValue;
+  mla_gemm_kernel<kDc><<<dim3(H, dv / kGemmN), dim3(256), 0, stream>>>(
+      o_lat, kDc, (long long)H * kDc, static_cast<const uint16_t*>(w_uv), dv, static_cast<uint16_t*>(out), dv,
+      (long long)H * dv, B, nullptr, H);
   return hipGetLastError();
 }
