@@ -137,7 +137,8 @@ struct DecodeArgs {
   int batch, n_heads, n_kv_heads, max_context;
   int head_chunks;             // chunks per kv head's query group
   int chunk_heads;             // query heads per chunk (group / head_chunks)
-  int n_wg;                    // persistent grid size W
+  int n_wg;                    // persistent grid size (launched)
+  int n_cus, wa, wb;           // partition weights: first n_cus workgroups wa, the rest wb
   float* ws_acc;               // [slot][GC][D]
   float* ws_ml;                // [slot][GC][2]
   int32_t* ws_cnt;             // [B * H_kv * chunks] arrival counters (self-resetting)
@@ -157,6 +158,15 @@ constexpr int kSegRows = KVC_SEG_ROWS;
 #endif
 static_assert(kSegRows >= 0 && kSegRows <= kMaxSegRows, "row space must stay below 2^31");
 
+// Row-space shares of the first workgroup on each CU and of the others.
+#ifndef KVC_SHARE_FIRST
+constexpr int kShareFirst = 1;
+constexpr int kShareRest = 1;
+#else
+constexpr int kShareFirst = KVC_SHARE_FIRST;
+constexpr int kShareRest = KVC_SHARE_REST;
+#endif
+
 // A piece that is part of a segment (only a workgroup's first and last
 // piece can be) is recorded while the workgroup streams on; at the end the
 // workgroup waits once for all of its partial stores, counts its pieces in,
@@ -169,26 +179,24 @@ struct SplitPiece {
 };
 
 template <typename T, int D, int SH>
-__device__ void finish_splits(const DecodeArgs& a, const SplitPiece* sp, int nsp, int* s_flag, long long R,
-                              int W) {
+__device__ void finish_splits(const DecodeArgs& a, const SplitPiece* sp, int nsp, int* s_flag,
+                              const Partition& part) {
   wait_stores();
   __syncthreads();
   if (threadIdx.x < nsp) {
     const SplitPiece& q = sp[threadIdx.x];
-    const int w0 = wg_of(q.seg_start, R, W);
-    const int w1 = wg_of(q.seg_start + q.n - 1, R, W);
+    const int w0 = part.of(q.seg_start);
+    const int w1 = part.of(q.seg_start + q.n - 1);
     const int old = __hip_atomic_fetch_add(a.ws_cnt + q.s, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_flag[threadIdx.x * 3 + 0] = (old == w1 - w0) ? 1 : 0;
     s_flag[threadIdx.x * 3 + 1] = w0;
     s_flag[threadIdx.x * 3 + 2] = w1 - w0 + 1;
   }
   __syncthreads();
-  // Merge in two rounds of loads: every piece's (m, l) into shared memory,
-  // the weights 2^(m_p - m*) and 1/l* per head, then each thread's output
-  // elements with all of their partial loads in flight together.
-  __shared__ float s_w[kMaxMerge * 16];  // m_p, then the weight of piece p (head-minor)
-  __shared__ float s_l[kMaxMerge * 16];
-  __shared__ float s_inv[16];
+  // Merge in one round of loads: each thread requests (m_p, l_p, acc_p) of
+  // its output elements for a batch of pieces at once and folds them into a
+  // running (maximum, denominator, sum), rescaling when a batch raises the
+  // maximum.
   const int gc = a.chunk_heads;
   constexpr int E = 2;  // output elements per thread and pass
   constexpr int K = 8;  // pieces per batch of loads
@@ -197,56 +205,56 @@ __device__ void finish_splits(const DecodeArgs& a, const SplitPiece* sp, int nsp
     const SplitPiece& q = sp[k];
     const int w0 = s_flag[k * 3 + 1];
     const int np = s_flag[k * 3 + 2];
-    auto entry = [&](int p, int h) { return ((size_t)(w0 + p + q.s)) * SH + h; };
-    for (int t = threadIdx.x; t < np * gc; t += kThreads) {
-      const int p = t / gc, h = t - p * gc;
-      s_w[t] = get(a.ws_ml + entry(p, h) * 2);
-      s_l[t] = get(a.ws_ml + entry(p, h) * 2 + 1);
-    }
-    __syncthreads();
-    if (threadIdx.x < gc) {
-      const int h = threadIdx.x;
-      float mx = -INFINITY;
-      for (int p = 0; p < np; ++p) mx = fmaxf(mx, s_w[p * gc + h]);
-      float lsum = 0.0f;
-      for (int p = 0; p < np; ++p) {
-        const float f = __builtin_amdgcn_exp2f(s_w[p * gc + h] - mx);
-        s_w[p * gc + h] = f;
-        lsum = fmaf(s_l[p * gc + h], f, lsum);
-      }
-      s_inv[h] = 1.0f / lsum;
-    }
-    __syncthreads();
     T* o = reinterpret_cast<T*>(a.out) + ((size_t)q.b * a.n_heads + q.h0) * D;
     for (int base = 0; base < gc * D; base += E * kThreads) {
-      float x[E];
+      int h[E], d[E];
 #pragma unroll
-      for (int e = 0; e < E; ++e) x[e] = 0.0f;
+      for (int e = 0; e < E; ++e) {
+        const int idx = min(base + e * kThreads + (int)threadIdx.x, gc * D - 1);
+        h[e] = idx / D;
+        d[e] = idx - h[e] * D;
+      }
+      float mx[E], ls[E], x[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        mx[e] = -INFINITY;
+        ls[e] = 0.0f;
+        x[e] = 0.0f;
+      }
       for (int p0 = 0; p0 < np; p0 += K) {
-        float aa[E][K];
+        float mm[E][K], ll[E][K], aa[E][K];
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+#pragma unroll
+          for (int i = 0; i < K; ++i) {
+            const size_t ent = ((size_t)(w0 + min(p0 + i, np - 1) + q.s)) * SH + h[e];
+            mm[e][i] = get(a.ws_ml + ent * 2);
+            ll[e][i] = get(a.ws_ml + ent * 2 + 1);
+            aa[e][i] = get(a.ws_acc + ent * D + d[e]);
+          }
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-          const int idx = min(base + e * kThreads + (int)threadIdx.x, gc * D - 1);
-          const int h = idx / D, d = idx - h * D;
+          float bm = mx[e];
 #pragma unroll
-          for (int i = 0; i < K; ++i) aa[e][i] = get(a.ws_acc + entry(min(p0 + i, np - 1), h) * D + d);
-        }
+          for (int i = 0; i < K; ++i) bm = (p0 + i < np) ? fmaxf(bm, mm[e][i]) : bm;
+          const float c = __builtin_amdgcn_exp2f(mx[e] - bm);  // 0 on the first batch (mx = -inf)
+          x[e] *= c;
+          ls[e] *= c;
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const int idx = min(base + e * kThreads + (int)threadIdx.x, gc * D - 1);
-          const int h = idx / D;
-#pragma unroll
-          for (int i = 0; i < K; ++i)
-            if (p0 + i < np) x[e] = fmaf(aa[e][i], s_w[(p0 + i) * gc + h], x[e]);
+          for (int i = 0; i < K; ++i) {
+            const float f = (p0 + i < np) ? __builtin_amdgcn_exp2f(mm[e][i] - bm) : 0.0f;
+            x[e] = fmaf(aa[e][i], f, x[e]);
+            ls[e] = fmaf(ll[e][i], f, ls[e]);
+          }
+          mx[e] = bm;
         }
       }
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         const int idx = base + e * kThreads + (int)threadIdx.x;
-        if (idx < gc * D) store_out(o + idx, x[e] * s_inv[idx / D]);
+        if (idx < gc * D) store_out(o + idx, x[e] / ls[e]);
       }
     }
-    __syncthreads();  // s_w, s_l and s_inv are reused by the next merge
     if (threadIdx.x == 0) __hip_atomic_store(a.ws_cnt + q.s, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
@@ -691,10 +699,10 @@ void gqa_decode_kernel(DecodeArgs a) {
     }
   }
 
-  const int W = effective_wg(a.n_wg, R, s_umax);
-  if (w >= W) return;
-  long long x = wg_lo(w, R, W);
-  const long long hi = wg_lo(w + 1, R, W);
+  const Partition part(R, a.n_wg, s_umax, a.n_cus, a.wa, a.wb);
+  if (w >= part.W) return;
+  long long x = part.lo(w);
+  const long long hi = part.lo(w + 1);
   if (x >= hi) return;
   __shared__ int s_flag[6];
   __shared__ SplitPiece split[2];  // a workgroup's first and last piece may be parts of segments
@@ -719,7 +727,7 @@ void gqa_decode_kernel(DecodeArgs a) {
     }
   });
   if (nsplit > 0)
-    finish_splits<typename P::Elem, P::kD, P::kSlotHeads>(a, split, nsplit, s_flag, R, W);
+    finish_splits<typename P::Elem, P::kD, P::kSlotHeads>(a, split, nsplit, s_flag, part);
 }
 
 template <class P, typename T, int D>
@@ -737,6 +745,9 @@ hipError_t launch_piece(const kvc_cache* c, DecodeArgs a, int chunk_heads, hipSt
   a.head_chunks = group / chunk_heads;
   a.n_wg = c->workgroups_forced > 0 ? c->workgroups_forced : resident * c->num_cus;
   if (a.n_wg > c->max_workgroups) a.n_wg = c->max_workgroups;
+  a.n_cus = c->num_cus;
+  a.wa = kShareFirst;
+  a.wb = kShareRest;
   gqa_decode_kernel<P><<<dim3(a.n_wg), dim3(kThreads), 0, stream>>>(a);
   return hipGetLastError();
 }

@@ -82,35 +82,48 @@ __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F7
 // virtual rows (none if n_b = 0) of which the last n_b are real: seg_rows
 // stands for the fixed start-up cost of a segment (query load, the first
 // tile's latency, the epilogue), so a workgroup whose range crosses into a
-// new segment is handed correspondingly fewer real rows. Workgroup w of W
-// takes rows [w R / W, (w + 1) R / W); the part of a segment inside one
-// workgroup is a "piece".
-
-__device__ __forceinline__ long long wg_lo(int w, long long R, int W) { return (long long)w * R / W; }
-
-// Workgroup whose row range contains row x of the row space.
-__device__ __forceinline__ int wg_of(long long x, long long R, int W) {
-  int w = (int)(x * W / R);
-  while (w + 1 < W && wg_lo(w + 1, R, W) <= x) ++w;
-  while (w > 0 && wg_lo(w, R, W) > x) --w;
-  return w;
-}
+// new segment is handed correspondingly fewer real rows. The workgroups
+// take consecutive ranges of the row space (Partition below); the part of a
+// segment inside one workgroup's range is a "piece".
 
 constexpr int kMaxSpan = 64;               // the longest segment spans <= kMaxSpan + 2 workgroups
 constexpr int kMaxMerge = kMaxSpan + 2;    // pieces of one segment, at most
 constexpr int kMinRowsPerWorkgroup = 64;   // and every workgroup gets >= 64 rows (no empty ranges)
 constexpr int kMaxSegRows = 1024;          // start-up rows allowed (the desc limits keep R < 2^31)
 
-// Workgroups that share the row space: the launched grid, capped so every
-// workgroup gets >= kMinRowsPerWorkgroup rows and every workgroup's range
-// is at least 1/kMaxSpan of the longest segment (u_max virtual rows), so a
-// segment is cut into at most kMaxMerge pieces.
-__device__ __forceinline__ int effective_wg(int n_wg, long long R, int u_max) {
-  long long w = n_wg;
-  w = min(w, max(1LL, R * kMaxSpan / max(u_max, 1)));
-  w = min(w, max(1LL, R / kMinRowsPerWorkgroup));
-  return (int)w;
-}
+// The split of the row space among the persistent workgroups. Workgroups
+// [0, C) (C = CUs: the first workgroup on each CU, which the CU favours when
+// it issues) take shares of weight wa, the rest shares of weight wb; with
+// wa = wb every workgroup takes R / W rows. Workgroup w takes
+// [lo(w), lo(w + 1)). The grid is capped so that even the narrowest share
+// has >= kMinRowsPerWorkgroup rows and >= 1/kMaxSpan of the longest segment
+// (u_max virtual rows), so a segment is cut into at most kMaxMerge pieces.
+struct Partition {
+  long long R;
+  int W, C, wa, wb;
+
+  __device__ __forceinline__ Partition(long long R_, int n_wg, int u_max, int C_, int wa_, int wb_)
+      : R(R_), W(1), C(C_), wa(wa_), wb(wb_) {
+    const long long narrow = R * min(wa, wb) / max(wa, wb);  // R as seen by the narrowest share
+    long long w = n_wg;
+    w = min(w, max(1LL, narrow * kMaxSpan / max(u_max, 1)));
+    w = min(w, max(1LL, narrow / kMinRowsPerWorkgroup));
+    W = (int)w;
+  }
+  __device__ __forceinline__ long long cum(int w) const {
+    return w <= C ? (long long)w * wa : (long long)C * wa + (long long)(w - C) * wb;
+  }
+  __device__ __forceinline__ long long lo(int w) const { return w >= W ? R : R * cum(w) / cum(W); }
+  // Workgroup whose range contains row x.
+  __device__ __forceinline__ int of(long long x) const {
+    const long long c = x * cum(W) / R;  // cumulative weight at x
+    int w = c <= (long long)C * wa ? (int)(c / wa) : C + (int)((c - (long long)C * wa) / wb);
+    w = min(max(w, 0), W - 1);
+    while (w + 1 < W && lo(w + 1) <= x) ++w;
+    while (w > 0 && lo(w) > x) --w;
+    return w;
+  }
+};
 
 // Prefix sums s_prefix[0..B] of u_b and the largest u_b, by the first wave
 // (64 sequences per pass, an inclusive shuffle scan within the wave and a

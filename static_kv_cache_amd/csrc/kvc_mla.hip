@@ -61,6 +61,13 @@ constexpr int kSegRowsMla = 160;             // start-up rows of a segment (see 
 constexpr float kLazyMfma = 64.0f;           // log2 headroom before the reference maximum moves
 static_assert(kTok * kRowBytes % (16 * kThreads) == 0, "tile must split evenly over the threads");
 static_assert(kSegRowsMla <= kMaxSegRows, "row space must stay below 2^31");
+#ifndef KVC_SHARE_FIRST
+constexpr int kShareFirstMla = 1;            // row-space shares of the first workgroup on each CU
+constexpr int kShareRestMla = 1;             // and of the others
+#else
+constexpr int kShareFirstMla = KVC_SHARE_FIRST;
+constexpr int kShareRestMla = KVC_SHARE_REST;
+#endif
 
 struct MlaArgs {
   const uint16_t* rows;        // layer rows [B][S][576]
@@ -74,6 +81,7 @@ struct MlaArgs {
   int batch, n_heads, max_context;
   int head_chunks, chunk_heads;  // H = head_chunks * chunk_heads, chunk_heads <= 16
   int n_wg;
+  int n_cus, wa, wb;           // partition weights: first n_cus workgroups wa, the rest wb
   int32_t* err_flag;
 };
 
@@ -249,11 +257,11 @@ __global__ __launch_bounds__(kThreads) void mla_split_kernel(MlaArgs a) {
                   blockIdx.x == 0);
   const int HC = a.head_chunks;
   const long long R = (long long)s_prefix[B] * HC;
-  const int W = effective_wg(a.n_wg, R, s_umax);
+  const Partition part(R, a.n_wg, s_umax, a.n_cus, a.wa, a.wb);
   const int w = blockIdx.x;
-  if (w >= W) return;
-  const long long x = wg_lo(w, R, W);
-  const long long hi = wg_lo(w + 1, R, W);
+  if (w >= part.W) return;
+  const long long x = part.lo(w);
+  const long long hi = part.lo(w + 1);
   if (x >= hi) return;
   for_each_piece(s_prefix, B, HC, kSegRowsMla, x, hi,
                  [&](int b, int hc, int r_begin, int r_end, int, long long) {
@@ -288,11 +296,11 @@ __global__ __launch_bounds__(kThreads) void mla_merge_kernel(MlaArgs a) {
     return;
   }
   const long long R = (long long)s_prefix[B] * HC;
-  const int W = effective_wg(a.n_wg, R, s_umax);
+  const Partition part(R, a.n_wg, s_umax, a.n_cus, a.wa, a.wb);
   const int n = u - kSegRowsMla;
   const long long real0 = (long long)s_prefix[b] * HC + (long long)hc * u + kSegRowsMla;
-  const int w0 = wg_of(real0, R, W);
-  const int np = wg_of(real0 + n - 1, R, W) - w0 + 1;
+  const int w0 = part.of(real0);
+  const int np = part.of(real0 + n - 1) - w0 + 1;
   const long long slot0 = (long long)w0 + seg;
   // This thread's partial columns for the first K pieces are requested
   // before the weights are worked out, so both loads overlap.
@@ -443,6 +451,9 @@ hipError_t kvc_launch_mla_attn(const kvc_cache* c, const void* rows_layer, const
   a.head_chunks = c->d.n_heads / a.chunk_heads;
   a.n_wg = c->workgroups_forced > 0 ? c->workgroups_forced : resident * c->num_cus;
   if (a.n_wg > c->max_workgroups) a.n_wg = c->max_workgroups;
+  a.n_cus = c->num_cus;
+  a.wa = kShareFirstMla;
+  a.wb = kShareRestMla;
   a.err_flag = c->err_flag;
   mla_split_kernel<<<dim3(a.n_wg), dim3(kThreads), 0, stream>>>(a);
   hipError_t e = hipGetLastError();
