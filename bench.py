@@ -1,9 +1,10 @@
 """Benchmark of the static KV-cache decode path on one MI355X.
 
 One step = one decode step of the Llama-3-8B-shaped GQA stack: for each of
-the 32 layers, the in-place append of the new token's K/V at cache_index
-(kvc_append) and single-query attention of all 32 query heads over each
-sequence's valid rows (kvc_decode_attn). Batch 16, H_kv = 8, d_h = 128,
+the 32 layers, the in-place append of the new token's K/V at cache_index and
+single-query attention of all 32 query heads over each sequence's valid rows,
+in one launch (kvc_append_decode_attn; the two-call form kvc_append +
+kvc_decode_attn is timed beside it). Batch 16, H_kv = 8, d_h = 128,
 max_context 4096, per-sequence valid_len ~ U[1024, 4096] (seeded), bf16
 storage with fp32 accumulation. All inputs are resident in HBM before the
 timed region; the step replays the same position (idempotent append) so
@@ -12,8 +13,9 @@ every step moves the same bytes. The 32 layers occupy 8 GiB, far above the
 
 Reported (one JSON line on stdout):
   value        KV GB/s = KV bytes read per step / step time (graph-replayed)
-  roofline     the decode kernel: algorithmic bytes per launch / its mean
-               duration from HIP events on its stream, against 8 TB/s
+  roofline     the layer kernel (append + decode attention): algorithmic bytes
+               per launch / its mean duration from HIP events on its stream,
+               against 8 TB/s
   cpu_baseline the float64 oracle timed on a bounded sample on the host
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
@@ -114,17 +116,24 @@ class Workload:
         p = 2
         self.kv_read_per_layer = self.sum_valid * 2 * Hkv * D * p
         self.decode_alg_bytes = (self.kv_read_per_layer + 2 * B * H * D * p + 8 * B)
-        self.append_bytes = 2 * (2 * B * Hkv * D * p) + 4 * B   # read + write of the new rows
-        self.kernel_name = f"gqa_decode_kernel<MfmaPiece<{D}>> (bf16 MFMA piece, d_h={D})"
+        self.append_bytes = 2 * (2 * B * Hkv * D * p)   # read + write of the new K and V rows
+        self.fused_alg_bytes = self.decode_alg_bytes + self.append_bytes
+        self.kernel_name = (f"gqa_decode_kernel<MfmaPiece<{D}>> (bf16 MFMA piece, d_h={D}), "
+                            f"launched by kvc_append_decode_attn")
 
     def layer_step(self, layer, ev=None):
-        self.cache.append(layer, self.kn[layer], self.vn[layer], self.ci)
+        """append + decode attention of one layer, one launch"""
         if ev is not None:
             ev[0].record()
-        self.cache.decode_attn(layer, self.q[layer], self.out[layer], valid_lens=self.valid,
-                               cache_index=self.ci, sm_scale=self.sm_scale)
+        self.cache.append_decode_attn(layer, self.kn[layer], self.vn[layer], self.q[layer], self.out[layer],
+                                      self.ci, self.sm_scale)
         if ev is not None:
             ev[1].record()
+
+    def layer_step_two_calls(self, layer):
+        self.cache.append(layer, self.kn[layer], self.vn[layer], self.ci)
+        self.cache.decode_attn(layer, self.q[layer], self.out[layer], valid_lens=self.valid,
+                               cache_index=self.ci, sm_scale=self.sm_scale)
 
     def decode(self, layer):
         self.cache.decode_attn(layer, self.q[layer], self.out[layer], valid_lens=self.valid,
@@ -133,6 +142,10 @@ class Workload:
     def step(self):
         for layer in range(self.L):
             self.layer_step(layer)
+
+    def step_two_calls(self):
+        for layer in range(self.L):
+            self.layer_step_two_calls(layer)
 
 
 class MlaWorkload:
@@ -287,6 +300,10 @@ def main():
         wl.step()
     ms_eager = time_steps(torch, wl.step, args.steps)
     log(f"bench: eager {ms_eager:.4f} ms/step")
+    for _ in range(args.warmup):
+        wl.step_two_calls()
+    ms_two = time_steps(torch, wl.step_two_calls, args.steps)
+    log(f"bench: eager, append and decode as two launches: {ms_two:.4f} ms/step")
 
     # --- per-kernel durations of the decode kernel (HIP events on its stream)
     L = wl.L
@@ -299,23 +316,28 @@ def main():
     torch.cuda.synchronize()
     durs = [a.elapsed_time(b) for a, b in evs]
     pair_ms = float(np.mean(durs))
-    log(f"bench: decode kernel, one event pair per launch: mean {pair_ms * 1e3:.2f} us over "
+    log(f"bench: layer kernel, one event pair per launch: mean {pair_ms * 1e3:.2f} us over "
         f"{len(durs)} launches (median {np.median(durs) * 1e3:.2f})")
-    # back-to-back decode launches over the 32 layers between one event pair:
-    # no other work between them, so the pair's own cost is spread over L launches
+    # back-to-back launches over the 32 layers between one event pair: no
+    # other work between them, so the pair's own cost is spread over L launches
     bursts = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(args.steps)]
     torch.cuda.synchronize()
-    for s0, s1 in bursts:
-        s0.record()
-        for layer in range(L):
-            wl.decode(layer)
-        s1.record()
-    torch.cuda.synchronize()
-    bdurs = [a.elapsed_time(b) / L for a, b in bursts]
-    decode_ms = float(np.mean(bdurs))
-    log(f"bench: decode kernel, back-to-back bursts of {L}: mean {decode_ms * 1e3:.2f} us per launch "
-        f"over {len(bdurs) * L} launches")
+    def burst(fn):
+        torch.cuda.synchronize()
+        for s0, s1 in bursts:
+            s0.record()
+            for layer in range(L):
+                fn(layer)
+            s1.record()
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) / L for a, b in bursts]))
+
+    fused_ms = burst(wl.layer_step)
+    log(f"bench: layer kernel (append + decode), back-to-back bursts of {L}: mean {fused_ms * 1e3:.2f} us "
+        f"per launch over {args.steps * L} launches")
+    decode_ms = burst(wl.decode)
+    log(f"bench: decode-only kernel, back-to-back bursts of {L}: mean {decode_ms * 1e3:.2f} us per launch")
 
     # --- graph replay of the whole step ---------------------------------
     ms_graph = None
@@ -339,13 +361,15 @@ def main():
     ms = ms_graph if ms_graph is not None else ms_eager
     kv_bytes_step = wl.kv_read_per_layer * L
     value = kv_bytes_step / (ms * 1e-3) / 1e9
-    achieved = wl.decode_alg_bytes / (decode_ms * 1e-3) / 1e9
+    achieved = wl.fused_alg_bytes / (fused_ms * 1e-3) / 1e9
     roof = dict(bound="hbm", achieved=round(achieved, 2), peak=HBM_PEAK_GBS, unit="GB/s",
                 frac=round(achieved / HBM_PEAK_GBS, 4), traffic=read_pmc_traffic(),
                 kernel=wl.kernel_name,
-                alg_bytes_per_launch=wl.decode_alg_bytes, mean_launch_us=round(decode_ms * 1e3, 3),
+                alg_bytes_per_launch=wl.fused_alg_bytes, mean_launch_us=round(fused_ms * 1e3, 3),
                 timing=f"HIP events on the launch stream, {args.steps} bursts of {L} back-to-back launches",
-                event_pair_us=round(pair_ms * 1e3, 3))
+                event_pair_us=round(pair_ms * 1e3, 3),
+                decode_only_us=round(decode_ms * 1e3, 3),
+                decode_only_achieved=round(wl.decode_alg_bytes / (decode_ms * 1e-3) / 1e9, 2))
     wg_forced = wl.cache.workgroups()[0]
     wl.cache.free()
     mla = None if args.no_mla else bench_mla(torch, max(5, args.steps // 2), 2)
@@ -367,12 +391,13 @@ def main():
         "layer_steps_per_s": round(L / (ms * 1e-3), 1),
         "decode_steps_per_s": round(1.0 / (ms * 1e-3), 2),
         "eager_ms_per_step": round(ms_eager, 5),
+        "eager_ms_per_step_two_launches": round(ms_two, 5),
         "config": {"workload": WORKLOAD, "n_layers": L, "batch": wl.B, "n_heads": wl.H,
                    "n_kv_heads": wl.Hkv, "head_dim": wl.D, "max_context": wl.S,
                    "valid_len": "U[1024,4096] seed 2", "sum_valid_len": wl.sum_valid,
                    "workgroups": wg_forced or "resident",
                    "launch": "hipgraph" if ms_graph is not None else "eager",
-                   "step": "32 x (append + decode attention)"},
+                   "step": "32 x kvc_append_decode_attn (append + decode attention, one launch per layer)"},
         "roofline": roof,
         "cpu_baseline": cpu,
         "mla": mla,

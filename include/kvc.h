@@ -165,6 +165,21 @@ kvc_status kvc_decode_attn(kvc_cache* cache, int32_t layer, const void* q, void*
                            const int32_t* valid_lens, const int32_t* cache_index,
                            float sm_scale, void* stream);
 
+/* One decode step of one GQA layer in one launch: the same result as
+ *   kvc_append(cache, layer, k_new, v_new, cache_index, 1, stream);
+ *   kvc_decode_attn(cache, layer, q, out, NULL, cache_index, sm_scale, stream);
+ * ("10.3 ...", section 5 step 2: append k_t, v_t, then attend rows 0..t),
+ * i.e. the new row is written at cache_index[b] and attended together with
+ * rows [0, cache_index[b]). k_new, v_new = [B][H_kv][1][d_h]; q, out as for
+ * kvc_decode_attn. The new row enters the attention straight from k_new /
+ * v_new, and the kernel writes it into the cache in the same launch, so the
+ * output bits equal those of the two calls. A sequence with cache_index[b]
+ * outside [0, max_context) is skipped (no write, zero output) and raises the
+ * device-range flag. Latent caches: KVC_ERR_UNSUPPORTED. */
+kvc_status kvc_append_decode_attn(kvc_cache* cache, int32_t layer, const void* k_new, const void* v_new,
+                                  const void* q, void* out, const int32_t* cache_index, float sm_scale,
+                                  void* stream);
+
 /* Full latent (MLA) decode step for an MLA cache ("10.3 ...", section 4.3;
  * "KV-Cache Mechanics", MHA vs GQA vs MLA comparison, "absorb" overhead):
  *   q~[b,h]  = [ W_UK[h]^T q_nope[b,h] ; q_rope[b,h] ]

@@ -143,7 +143,35 @@ struct DecodeArgs {
   float* ws_ml;                // [slot][GC][2]
   int32_t* ws_cnt;             // [B * H_kv * chunks] arrival counters (self-resetting)
   int32_t* err_flag;
+  // Fused append (null for plain decode): the new rows [B][H_kv][1][D]. Row
+  // n_b - 1 = cache_index[b] of every segment is then taken from here, not
+  // from the cache, and written into the cache by the piece that ends there.
+  const void* k_new;
+  const void* v_new;
 };
+
+// Fused append: the piece of segment (b, g, chunk) that ends at the
+// segment's last row holds the new row (else -1). Chunk 0 of that piece
+// also writes the new K and V rows into the cache. No piece uses the cache's
+// copy of row n - 1 in this launch (the matrix-core piece never loads it;
+// the vector piece may load it and then replaces it with the new row), so
+// the write needs no ordering against the readers.
+template <typename T, int D>
+__device__ __forceinline__ int fused_row(const DecodeArgs& a, int b, int g, int chunk, int r_end, int n) {
+  if (!a.k_new || r_end != n) return -1;
+  if (chunk == 0) {
+    constexpr int kVecs = D * (int)sizeof(T) / 16;  // 16-byte vectors per row
+    const size_t src = ((size_t)b * a.n_kv_heads + g) * kVecs;
+    const size_t dst = (((size_t)b * a.n_kv_heads + g) * a.max_context + (n - 1)) * kVecs;
+    for (int i = threadIdx.x; i < 2 * kVecs; i += 64 * kWaves) {
+      const bool kk = i < kVecs;
+      const int v = kk ? i : i - kVecs;
+      const uint4 x = reinterpret_cast<const uint4*>(kk ? a.k_new : a.v_new)[src + v];
+      reinterpret_cast<uint4*>(const_cast<void*>(kk ? a.k : a.v))[dst + v] = x;
+    }
+  }
+  return n - 1;
+}
 
 // Start-up cost of a segment in rows: a workgroup that begins a segment
 // pays for its q load, the first tile's latency and the epilogue whatever
@@ -284,7 +312,7 @@ struct ValuPiece {
   // Rows [r_begin, r_end) of segment (b, g, chunk). Writes the normalised
   // output when the piece is the whole segment, else the partial of `slot`.
   static __device__ __forceinline__ void run(const DecodeArgs& a, Smem& sm, int b, int g, int chunk, int r_begin,
-                             int r_end, bool whole, long long slot) {
+                             int r_end, int n, bool whole, long long slot) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int rs = lane / LPR;          // row slot of this lane
@@ -310,6 +338,9 @@ struct ValuPiece {
     const size_t row0 = ((size_t)b * a.n_kv_heads + g) * (size_t)a.max_context;
     const uint4* kp = reinterpret_cast<const uint4*>(a.k) + row0 * LPR + vec;
     const uint4* vp = reinterpret_cast<const uint4*>(a.v) + row0 * LPR + vec;
+    const int fresh = fused_row<T, D>(a, b, g, chunk, r_end, n);  // row taken from the new rows, or -1
+    const uint4* knp = reinterpret_cast<const uint4*>(a.k_new) + ((size_t)b * a.n_kv_heads + g) * LPR + vec;
+    const uint4* vnp = reinterpret_cast<const uint4*>(a.v_new) + ((size_t)b * a.n_kv_heads + g) * LPR + vec;
 
     // Tile loads never leave [r_begin, r_end): rows past the end are clamped
     // to the last valid row (and masked in the softmax), so the next tile can
@@ -320,6 +351,17 @@ struct ValuPiece {
         const int rc = min(base + u * RPI + rs, r_end - 1);
         kr[u] = kp[(size_t)rc * LPR];
         vr[u] = vp[(size_t)rc * LPR];
+      }
+      // rows at or past `fresh` clamp to it: every such lane takes the new
+      // row (the cache row is stale until this launch writes it)
+      if (fresh >= 0 && base + TILE > fresh) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          if (min(base + u * RPI + rs, r_end - 1) == fresh) {
+            kr[u] = *knp;
+            vr[u] = *vnp;
+          }
+        }
       }
     };
     // One tile: raw scores q.k, then the online softmax in log2 units with
@@ -495,7 +537,7 @@ struct MfmaPiece {
   };
 
   static __device__ __forceinline__ void run(const DecodeArgs& a, Smem& sm, int b, int kvg, int chunk,
-                                             int r_begin, int r_end, bool whole, long long slot) {
+                                             int r_begin, int r_end, int n, bool whole, long long slot) {
     b = uniform(b);
     kvg = uniform(kvg);
     chunk = uniform(chunk);
@@ -537,10 +579,16 @@ struct MfmaPiece {
     // (sequence, kv head): loads of rows past the end (the tail of the last
     // tile, prefetches past the piece) return zeros without touching memory,
     // and their scores are masked below.
-    const __amdgpu_buffer_rsrc_t kres = buffer_rsrc(kbase, r_end * (2 * D));
-    const __amdgpu_buffer_rsrc_t vres = buffer_rsrc(vbase, r_end * (2 * D));
+    // Fused append: the new row `fresh` lies outside the resources (it reads
+    // as zeros) and is taken from k_new / v_new by the lanes that hold it.
+    const int fresh = uniform(fused_row<uint16_t, D>(a, b, kvg, chunk, r_end, n));
+    const int r_cache = fresh >= 0 ? fresh : r_end;  // rows read from the cache
+    const __amdgpu_buffer_rsrc_t kres = buffer_rsrc(kbase, r_cache * (2 * D));
+    const __amdgpu_buffer_rsrc_t vres = buffer_rsrc(vbase, r_cache * (2 * D));
     const int koff = j * (2 * D) + 16 * g;  // K row base + j, dims 8g.. of each 32-dim step
     const int voff = lane * 16;             // V tile as contiguous 16-byte chunks
+    const uint16_t* knew = reinterpret_cast<const uint16_t*>(a.k_new) + ((size_t)b * a.n_kv_heads + kvg) * D;
+    const uint16_t* vnew = reinterpret_cast<const uint16_t*>(a.v_new) + ((size_t)b * a.n_kv_heads + kvg) * D;
 
     auto load_tile = [&](int base, bf16x8_t (&kr)[KS], u32x4_t (&vr)[VCH]) {
       const int kb = base * (2 * D) + koff;
@@ -550,6 +598,17 @@ struct MfmaPiece {
       const int vb = base * (2 * D) + voff;
 #pragma unroll
       for (int i = 0; i < VCH; ++i) vr[i] = __builtin_amdgcn_raw_buffer_load_b128(vres, vb + 1024 * i, 0, 0);
+      if (fresh >= base && fresh < base + TR) {  // this tile holds the new row
+        if (base + j == fresh) {
+#pragma unroll
+          for (int k = 0; k < KS; ++k) kr[k] = *reinterpret_cast<const bf16x8_t*>(knew + 32 * k + 8 * g);
+        }
+#pragma unroll
+        for (int i = 0; i < VCH; ++i) {
+          const int f = i * 64 + lane;
+          if (base + f / CPR == fresh) vr[i] = *reinterpret_cast<const u32x4_t*>(vnew + 8 * (f % CPR));
+        }
+      }
     };
     auto use_tile = [&](int base, const bf16x8_t (&kr)[KS], const u32x4_t (&vr)[VCH]) {
       // stage V row-major in LDS
@@ -684,7 +743,7 @@ void gqa_decode_kernel(DecodeArgs a) {
   const int B = a.batch;
   const int t = threadIdx.x;
   build_row_space(a.valid_lens, a.cache_index, B, a.max_context, kSegRows, s_prefix, &s_umax, a.err_flag,
-                  blockIdx.x == 0);
+                  blockIdx.x == 0, a.k_new ? 1 : 0);
 
   const int HC = a.n_kv_heads * a.head_chunks;  // segments per sequence
   const long long R = (long long)s_prefix[B] * HC;
@@ -714,7 +773,7 @@ void gqa_decode_kernel(DecodeArgs a) {
     const bool whole = r_begin == 0 && r_end == n;
     const int kvg = hc / a.head_chunks;
     const int chunk = hc % a.head_chunks;
-    P::run(a, sm, b, kvg, chunk, r_begin, r_end, whole, (long long)w + s);
+    P::run(a, sm, b, kvg, chunk, r_begin, r_end, n, whole, (long long)w + s);
     if (!whole && nsplit < 2) {
       if (threadIdx.x == 0) {  // read after the barriers in finish_splits
         split[nsplit].s = s;
@@ -775,7 +834,8 @@ hipError_t launch_f32(const kvc_cache* c, const DecodeArgs& a, hipStream_t st) {
 
 hipError_t kvc_launch_gqa_decode(const kvc_cache* c, const void* k_layer, const void* v_layer,
                                  const void* q, void* out, const int32_t* valid_lens,
-                                 const int32_t* cache_index, float sm_scale, hipStream_t stream) {
+                                 const int32_t* cache_index, float sm_scale, hipStream_t stream,
+                                 const void* k_new, const void* v_new) {
   if (c->d.batch > KVC_MAX_BATCH || (long long)c->d.batch * c->d.n_heads > 0x7fffffffLL)
     return hipErrorInvalidValue;
   DecodeArgs a;
@@ -797,6 +857,8 @@ hipError_t kvc_launch_gqa_decode(const kvc_cache* c, const void* k_layer, const 
   a.ws_ml = c->ws_ml;
   a.ws_cnt = c->ws_cnt;
   a.err_flag = c->err_flag;
+  a.k_new = k_new;
+  a.v_new = v_new;
   const bool bf16 = c->d.dtype == KVC_BF16;
   switch (c->d.head_dim) {
     case 32: return bf16 ? launch_bf16<32>(c, a, stream) : launch_f32<32>(c, a, stream);

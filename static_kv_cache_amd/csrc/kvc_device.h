@@ -49,12 +49,13 @@ __device__ __forceinline__ void store_out(uint16_t* p, float f) { *p = bf16_rne(
 __device__ __forceinline__ void store_out(float* p, float f) { *p = f; }
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
-// Valid rows of sequence b as the kernels use them: out-of-range lengths
-// count as 0 (the sequence is skipped and flagged).
+// Valid rows of sequence b as the kernels use them: lengths outside
+// [min_rows, max_context] count as 0 (the sequence is skipped and flagged).
+// min_rows is 1 when the launch also appends the row at cache_index[b].
 __device__ __forceinline__ int seq_rows(const int32_t* valid_lens, const int32_t* cache_index, int b,
-                                        int max_context, bool* bad) {
+                                        int max_context, int min_rows, bool* bad) {
   const int n = valid_lens ? valid_lens[b] : cache_index[b] + 1;
-  *bad = n < 0 || n > max_context;
+  *bad = n < min_rows || n > max_context;
   return *bad ? 0 : n;
 }
 
@@ -132,7 +133,8 @@ struct Partition {
 // *err_flag when flag_errors is set.
 __device__ __forceinline__ void build_row_space(const int32_t* valid_lens, const int32_t* cache_index, int B,
                                                 int max_context, int seg_rows, int32_t* s_prefix,
-                                                int32_t* s_umax, int32_t* err_flag, bool flag_errors) {
+                                                int32_t* s_umax, int32_t* err_flag, bool flag_errors,
+                                                int min_rows = 0) {
   const int t = threadIdx.x;
   if (t < 64) {
     int carry = 0, umax = 0;
@@ -141,7 +143,7 @@ __device__ __forceinline__ void build_row_space(const int32_t* valid_lens, const
       int n = 0;
       if (b < B) {
         bool bad;
-        n = seq_rows(valid_lens, cache_index, b, max_context, &bad);
+        n = seq_rows(valid_lens, cache_index, b, max_context, min_rows, &bad);
         if (bad && flag_errors) atomicOr(err_flag, 1);
       }
       int x = n > 0 ? n + seg_rows : 0;

@@ -50,9 +50,12 @@ hipError_t kvc_launch_copy_rows(const void* src_k, const void* src_v, uint8_t* d
                                 hipStream_t stream);
 
 // Persistent split-context GQA decode (pieces merged in the same kernel).
+// With k_new / v_new (and valid_lens null) the launch also appends the new
+// row at cache_index and attends it from k_new / v_new.
 hipError_t kvc_launch_gqa_decode(const kvc_cache* c, const void* k_layer, const void* v_layer,
                                  const void* q, void* out, const int32_t* valid_lens,
-                                 const int32_t* cache_index, float sm_scale, hipStream_t stream);
+                                 const int32_t* cache_index, float sm_scale, hipStream_t stream,
+                                 const void* k_new = nullptr, const void* v_new = nullptr);
 
 // Latent (MLA) decode over absorbed queries q_abs [B][H][d_c + d_R] (bf16)
 // into out_lat [B][H][d_c] (bf16).

@@ -54,6 +54,7 @@ _SIGS = {
     "kvc_append": [_p, _i32, _p, _p, _p, _i32, _p],
     "kvc_decode_attn": [_p, _i32, _p, _p, _p, _p, ctypes.c_float, _p],
     "kvc_mla_decode": [_p, _i32, _p, _p, _p, _p, _p, _p, _p, ctypes.c_float, _p],
+    "kvc_append_decode_attn": [_p, _i32, _p, _p, _p, _p, _p, ctypes.c_float, _p],
     "kvc_set_workgroups": [_p, _i32],
     "kvc_get_workgroups": [_p, ctypes.POINTER(_i32), ctypes.POINTER(_i32)],
     "kvc_check": [_p, _p],
@@ -263,6 +264,17 @@ class Cache:
             raise ValueError("sm_scale is required")
         _call("kvc_decode_attn", self.handle, layer, qp, op, self._idx(valid_lens, "valid_lens"),
               self._idx(cache_index, "cache_index"), float(sm_scale), _stream(self.device))
+
+    def append_decode_attn(self, layer, k_new, v_new, q, out, cache_index, sm_scale):
+        """One launch: append the new row at cache_index, then attend rows
+        [0, cache_index + 1) (kvc_append_decode_attn; GQA caches)."""
+        d = self.desc
+        shape = (d.batch, d.n_kv_heads, 1, d.head_dim)
+        kp, vp = self._check(k_new, shape, name="k_new"), self._check(v_new, shape, name="v_new")
+        qp = self._check(q, (d.batch, d.n_heads, d.head_dim), name="q")
+        op = self._check(out, (d.batch, d.n_heads, d.head_dim), name="out")
+        _call("kvc_append_decode_attn", self.handle, layer, kp, vp, qp, op, self._idx(cache_index, "cache_index"),
+              float(sm_scale), _stream(self.device))
 
     def mla_decode(self, layer, q_nope, q_rope, w_uk, w_uv, out, valid_lens=None, cache_index=None,
                    sm_scale=None):
