@@ -151,26 +151,28 @@ struct DecodeArgs {
 };
 
 // Fused append: the piece of segment (b, g, chunk) that ends at the
-// segment's last row holds the new row (else -1). Chunk 0 of that piece
-// also writes the new K and V rows into the cache. No piece uses the cache's
-// copy of row n - 1 in this launch (the matrix-core piece never loads it;
-// the vector piece may load it and then replaces it with the new row), so
-// the write needs no ordering against the readers.
+// segment's last row holds the new row (else -1).
+__device__ __forceinline__ int fused_row(const DecodeArgs& a, int r_end, int n) {
+  return (a.k_new && r_end == n) ? n - 1 : -1;
+}
+
+// ... and chunk 0 of that piece writes the new K and V rows into the cache
+// (after its tile loop, so the copy does not delay the first loads). No
+// piece uses the cache's copy of row n - 1 in this launch (the matrix-core
+// piece never loads it; the vector piece may load it and then replaces it
+// with the new row), so the write needs no ordering against the readers.
 template <typename T, int D>
-__device__ __forceinline__ int fused_row(const DecodeArgs& a, int b, int g, int chunk, int r_end, int n) {
-  if (!a.k_new || r_end != n) return -1;
-  if (chunk == 0) {
-    constexpr int kVecs = D * (int)sizeof(T) / 16;  // 16-byte vectors per row
-    const size_t src = ((size_t)b * a.n_kv_heads + g) * kVecs;
-    const size_t dst = (((size_t)b * a.n_kv_heads + g) * a.max_context + (n - 1)) * kVecs;
-    for (int i = threadIdx.x; i < 2 * kVecs; i += 64 * kWaves) {
-      const bool kk = i < kVecs;
-      const int v = kk ? i : i - kVecs;
-      const uint4 x = reinterpret_cast<const uint4*>(kk ? a.k_new : a.v_new)[src + v];
-      reinterpret_cast<uint4*>(const_cast<void*>(kk ? a.k : a.v))[dst + v] = x;
-    }
+__device__ __forceinline__ void fused_write(const DecodeArgs& a, int b, int g, int chunk, int fresh) {
+  if (fresh < 0 || chunk != 0) return;
+  constexpr int kVecs = D * (int)sizeof(T) / 16;  // 16-byte vectors per row
+  const size_t src = ((size_t)b * a.n_kv_heads + g) * kVecs;
+  const size_t dst = (((size_t)b * a.n_kv_heads + g) * a.max_context + fresh) * kVecs;
+  for (int i = threadIdx.x; i < 2 * kVecs; i += 64 * kWaves) {
+    const bool kk = i < kVecs;
+    const int v = kk ? i : i - kVecs;
+    const uint4 x = reinterpret_cast<const uint4*>(kk ? a.k_new : a.v_new)[src + v];
+    reinterpret_cast<uint4*>(const_cast<void*>(kk ? a.k : a.v))[dst + v] = x;
   }
-  return n - 1;
 }
 
 // Start-up cost of a segment in rows: a workgroup that begins a segment
@@ -338,7 +340,7 @@ struct ValuPiece {
     const size_t row0 = ((size_t)b * a.n_kv_heads + g) * (size_t)a.max_context;
     const uint4* kp = reinterpret_cast<const uint4*>(a.k) + row0 * LPR + vec;
     const uint4* vp = reinterpret_cast<const uint4*>(a.v) + row0 * LPR + vec;
-    const int fresh = fused_row<T, D>(a, b, g, chunk, r_end, n);  // row taken from the new rows, or -1
+    const int fresh = fused_row(a, r_end, n);  // row taken from the new rows, or -1
     const uint4* knp = reinterpret_cast<const uint4*>(a.k_new) + ((size_t)b * a.n_kv_heads + g) * LPR + vec;
     const uint4* vnp = reinterpret_cast<const uint4*>(a.v_new) + ((size_t)b * a.n_kv_heads + g) * LPR + vec;
 
@@ -437,6 +439,7 @@ struct ValuPiece {
       use_any(base + stride, kb, vb);
     }
 
+    fused_write<T, D>(a, b, g, chunk, fresh);
     // Combine the wave's row slots (lanes with the same vector index).
 #pragma unroll
     for (int j = 0; j < GC; ++j) {
@@ -553,16 +556,8 @@ struct MfmaPiece {
     const float scale_log2 = a.scale_log2;
 
     // q as the B operand: column j is head h0 + j, zero past the chunk
+    // (loaded after the first tiles are requested, so the two latencies overlap)
     bf16x8_t qb[KS];
-    const bool real = j < gc;
-    const uint16_t* qh =
-        reinterpret_cast<const uint16_t*>(a.q) + ((size_t)b * a.n_heads + h0 + (real ? j : 0)) * D;
-#pragma unroll
-    for (int k = 0; k < KS; ++k) {
-      u32x4_t v = *reinterpret_cast<const u32x4_t*>(qh + 32 * k + 8 * g);
-      v = real ? v : u32x4_t{0u, 0u, 0u, 0u};
-      qb[k] = __builtin_bit_cast(bf16x8_t, v);
-    }
 
     f32x4_t o[NB];
 #pragma unroll
@@ -581,7 +576,7 @@ struct MfmaPiece {
     // and their scores are masked below.
     // Fused append: the new row `fresh` lies outside the resources (it reads
     // as zeros) and is taken from k_new / v_new by the lanes that hold it.
-    const int fresh = uniform(fused_row<uint16_t, D>(a, b, kvg, chunk, r_end, n));
+    const int fresh = uniform(fused_row(a, r_end, n));
     const int r_cache = fresh >= 0 ? fresh : r_end;  // rows read from the cache
     const __amdgpu_buffer_rsrc_t kres = buffer_rsrc(kbase, r_cache * (2 * D));
     const __amdgpu_buffer_rsrc_t vres = buffer_rsrc(vbase, r_cache * (2 * D));
@@ -674,6 +669,17 @@ struct MfmaPiece {
     u32x4_t vbuf[NBUF][VCH];
 #pragma unroll
     for (int i = 0; i < NBUF - 1; ++i) load_tile(base + i * stride, kbuf[i], vbuf[i]);
+    {
+      const bool real = j < gc;
+      const uint16_t* qh =
+          reinterpret_cast<const uint16_t*>(a.q) + ((size_t)b * a.n_heads + h0 + (real ? j : 0)) * D;
+#pragma unroll
+      for (int k = 0; k < KS; ++k) {
+        u32x4_t v = *reinterpret_cast<const u32x4_t*>(qh + 32 * k + 8 * g);
+        v = real ? v : u32x4_t{0u, 0u, 0u, 0u};
+        qb[k] = __builtin_bit_cast(bf16x8_t, v);
+      }
+    }
     for (; base < r_end; base += NBUF * stride) {
 #pragma unroll
       for (int i = 0; i < NBUF; ++i) {
@@ -682,6 +688,7 @@ struct MfmaPiece {
       }
     }
 
+    fused_write<uint16_t, D>(a, b, kvg, chunk, fresh);
     // denominators: sum the lane shares of each head column
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);

@@ -102,15 +102,9 @@ __device__ __forceinline__ void mla_piece(const MlaArgs& a, unsigned char* tile,
   const float scale_log2 = a.scale_log2;
 
   // q~ as the B operand of this wave's quarter of the 576 dims (k steps of
-  // 16): column j is head h0 + j, zero past the chunk
+  // 16): column j is head h0 + j, zero past the chunk (loaded after the
+  // first tiles are requested, so the two latencies overlap)
   s16x4_t qb[kQS];
-  const bool real = j < gc;
-  const uint16_t* qh = a.q_abs + ((size_t)b * a.n_heads + h0 + (real ? j : 0)) * kRow + kQDims * wave + 4 * g;
-#pragma unroll
-  for (int k = 0; k < kQS; ++k) {
-    s16x4_t v = *reinterpret_cast<const s16x4_t*>(qh + 16 * k);
-    qb[k] = real ? v : s16x4_t{0, 0, 0, 0};
-  }
 
   f32x4_t o[kNB];
 #pragma unroll
@@ -212,6 +206,15 @@ __device__ __forceinline__ void mla_piece(const MlaArgs& a, unsigned char* tile,
   u32x4_t st0[kVec], st1[kVec];
   load(st0, r_begin);
   load(st1, r_begin + kTok);
+  {
+    const bool real = j < gc;
+    const uint16_t* qh = a.q_abs + ((size_t)b * a.n_heads + h0 + (real ? j : 0)) * kRow + kQDims * wave + 4 * g;
+#pragma unroll
+    for (int k = 0; k < kQS; ++k) {
+      s16x4_t v = *reinterpret_cast<const s16x4_t*>(qh + 16 * k);
+      qb[k] = real ? v : s16x4_t{0, 0, 0, 0};
+    }
+  }
   for (int t0 = r_begin; t0 < r_end; t0 += 2 * kTok) {
     __syncthreads();  // every wave is done with the previous tile
     stage(st0);
