@@ -54,6 +54,8 @@ def parse():
     p.add_argument("--cpu-repeats", type=int, default=100)
     p.add_argument("--eager-only", action="store_true", help="skip the graph-replay leg")
     p.add_argument("--no-mla", action="store_true", help="skip the latent (MLA) leg")
+    p.add_argument("--mla-workgroups", type=int, default=0,
+                   help="force the latent leg's persistent grid size (0 = device default)")
     p.add_argument("--workgroups", type=int, default=0,
                    help="force the persistent attention grid size (0 = device default)")
     return p.parse_args()
@@ -199,12 +201,14 @@ class MlaWorkload:
                               valid_lens=self.valid, sm_scale=self.sm_scale)
 
 
-def bench_mla(torch, steps, warmup):
+def bench_mla(torch, steps, warmup, workgroups=0):
     """Latent attention alone (kvc_decode_attn on the latent cache: split +
     merge kernels) and the whole latent step (append + kvc_mla_decode:
     absorb, split, merge, up-projection), per layer, from HIP events around
     bursts of back-to-back launches over the rotated layers."""
     wl = MlaWorkload(torch, torch.device("cuda:0"))
+    if workgroups:
+        wl.cache.set_workgroups(workgroups)
     L = wl.L
 
     def burst(fn):
@@ -372,7 +376,7 @@ def main():
                 decode_only_achieved=round(wl.decode_alg_bytes / (decode_ms * 1e-3) / 1e9, 2))
     wg_forced = wl.cache.workgroups()[0]
     wl.cache.free()
-    mla = None if args.no_mla else bench_mla(torch, max(5, args.steps // 2), 2)
+    mla = None if args.no_mla else bench_mla(torch, max(5, args.steps // 2), 2, args.mla_workgroups)
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl, args.cpu_repeats)
     line = {
         "metric": METRIC,

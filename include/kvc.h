@@ -196,7 +196,7 @@ kvc_status kvc_mla_decode(kvc_cache* cache, int32_t layer, const void* q_nope, c
                           float sm_scale, void* stream);
 
 /* Force the number of persistent workgroups attention launches (0 restores
- * the default: as many as the device keeps resident at once). The rows of
+ * the default: one per compute unit). The rows of
  * all sequences and kv heads are divided evenly among them, so this only
  * changes how the context is partitioned and the rounding order of the
  * result. n must be in [0, *max_n of kvc_get_workgroups]. Host only. */

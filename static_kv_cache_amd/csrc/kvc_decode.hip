@@ -10,13 +10,13 @@
 //
 // How (flash-decoding style, exact up to rounding order):
 //  - Work space. A "segment" is the valid rows [0, n_b) of one (sequence,
-//    kv head, head chunk); segments are laid end to end in one row space of
-//    R = sum_b n_b * H_kv * chunks rows. The grid is persistent: exactly as
-//    many 256-thread workgroups as the chip keeps resident, and workgroup w
-//    takes rows [w R / W, (w + 1) R / W) of that space (stream-K style), so
-//    every workgroup streams the same number of rows whatever the ragged
-//    valid lengths are, in one round. The part of a segment inside one
-//    workgroup (a "piece") is processed as a unit.
+//    kv head, head chunk); segments are laid end to end in one row space
+//    (each with a fixed number of start-up rows in front, see kSegRows).
+//    The grid is persistent: one 256-thread workgroup per CU by default, and
+//    the workgroups take consecutive equal ranges of that space (stream-K
+//    style), so every workgroup streams about the same number of rows
+//    whatever the ragged valid lengths are, in one round. The part of a
+//    segment inside one workgroup (a "piece") is processed as a unit.
 //  - A piece is streamed ONCE and applied to all query heads of its head
 //    chunk. bf16 caches (MfmaPiece): each wave takes 16-row tiles in turn;
 //    q.k is one v_mfma_f32_16x16x32_bf16 per 32 dims with the 16 K rows as
@@ -798,18 +798,13 @@ void gqa_decode_kernel(DecodeArgs a) {
 
 template <class P, typename T, int D>
 hipError_t launch_piece(const kvc_cache* c, DecodeArgs a, int chunk_heads, hipStream_t stream) {
-  static int resident = 0;  // workgroups per CU this kernel keeps resident
-  if (resident == 0) {
-    int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, gqa_decode_kernel<P>, kThreads, 0) != hipSuccess ||
-        nb < 1)
-      nb = 1;
-    resident = nb;
-  }
   const int group = c->d.n_heads / c->d.n_kv_heads;
   a.chunk_heads = chunk_heads;
   a.head_chunks = group / chunk_heads;
-  a.n_wg = c->workgroups_forced > 0 ? c->workgroups_forced : resident * c->num_cus;
+  // One workgroup per CU by default: measured faster than filling every CU
+  // with the two workgroups it could hold (fewer pieces to merge, and no
+  // second workgroup competing for the CU's issue slots and LDS).
+  a.n_wg = c->workgroups_forced > 0 ? c->workgroups_forced : c->num_cus;
   if (a.n_wg > c->max_workgroups) a.n_wg = c->max_workgroups;
   a.n_cus = c->num_cus;
   a.wa = kShareFirst;

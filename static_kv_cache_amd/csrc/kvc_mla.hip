@@ -431,13 +431,6 @@ __global__ __launch_bounds__(256) void mla_gemm_kernel(const uint16_t* __restric
 hipError_t kvc_launch_mla_attn(const kvc_cache* c, const void* rows_layer, const void* q_abs, void* out_lat,
                                const int32_t* valid_lens, const int32_t* cache_index, float sm_scale,
                                hipStream_t stream) {
-  static int resident = 0;  // workgroups per CU the split kernel keeps resident
-  if (resident == 0) {
-    int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, mla_split_kernel, kThreads, 0) != hipSuccess || nb < 1)
-      nb = 1;
-    resident = nb;
-  }
   MlaArgs a;
   a.rows = static_cast<const uint16_t*>(rows_layer);
   a.q_abs = static_cast<const uint16_t*>(q_abs);
@@ -452,7 +445,7 @@ hipError_t kvc_launch_mla_attn(const kvc_cache* c, const void* rows_layer, const
   a.max_context = c->d.max_context;
   a.chunk_heads = c->d.n_heads <= kSlotHeads ? c->d.n_heads : kSlotHeads;
   a.head_chunks = c->d.n_heads / a.chunk_heads;
-  a.n_wg = c->workgroups_forced > 0 ? c->workgroups_forced : resident * c->num_cus;
+  a.n_wg = c->workgroups_forced > 0 ? c->workgroups_forced : c->num_cus;  // one per CU (measured best)
   if (a.n_wg > c->max_workgroups) a.n_wg = c->max_workgroups;
   a.n_cus = c->num_cus;
   a.wa = kShareFirstMla;
