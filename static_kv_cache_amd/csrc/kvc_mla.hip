@@ -134,15 +134,22 @@ __device__ __forceinline__ void mla_piece(const MlaArgs& a, unsigned char* tile,
   auto use_tile = [&](int t0) {
     // this wave's partial scores over its 144 dims, two 16-row blocks
     f32x4_t sp[2];
+    // all A fragments of the tile are requested before the first product
+    s16x4_t av[2][kQS];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const unsigned char* arow = tile + (16 * tb + j) * kStride + 2 * kQDims * wave + 8 * g;
+#pragma unroll
+      for (int k = 0; k < kQS; ++k) av[tb][k] = *reinterpret_cast<const s16x4_t*>(arow + 32 * k);
+    }
+    // keep the reads ahead of the products (the scheduler would otherwise
+    // pair each read with its product and wait out every LDS latency)
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
       sp[tb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-      const unsigned char* arow = tile + (16 * tb + j) * kStride + 2 * kQDims * wave + 8 * g;
 #pragma unroll
-      for (int k = 0; k < kQS; ++k) {
-        const s16x4_t av = *reinterpret_cast<const s16x4_t*>(arow + 32 * k);
-        sp[tb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, qb[k], sp[tb], 0, 0, 0);
-      }
+      for (int k = 0; k < kQS; ++k) sp[tb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av[tb][k], qb[k], sp[tb], 0, 0, 0);
       sred[(wave * 2 + tb) * 64 + lane] = sp[tb];
     }
     __syncthreads();  // partial scores visible
@@ -249,8 +256,9 @@ __device__ __forceinline__ void mla_piece(const MlaArgs& a, unsigned char* tile,
   __syncthreads();  // the tile is reused by the next piece
 }
 
-// Persistent latent attention: grid = W workgroups of 256 threads.
-__global__ __launch_bounds__(kThreads) void mla_split_kernel(MlaArgs a) {
+// Persistent latent attention: grid = W workgroups of 256 threads, one per
+// CU by default, so each wave may use a whole SIMD's register file.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void mla_split_kernel(MlaArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char tile[kTok * kStride];
   __shared__ f32x4_t sred[kWaves * 2 * 64];
   __shared__ int32_t s_prefix[KVC_MAX_BATCH + 1];
