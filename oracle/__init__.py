@@ -26,6 +26,7 @@ codec         bf16 / fp32 stored-bit decoding to float64
 buffer        bit-exact model of the static cache buffer and its append
 attention     decode attention (plain definition) and no-cache causal attention
 mla           latent (MLA) decode, materialised and absorbed forms
+quant         int8 storage with a float32 scale per row: codes, dequantisation, the cache model
 
 Parity status: every function here has a pin in ``tests/test_oracle_*.py``
 (printed worked examples, closed forms, invariants, library routines);
