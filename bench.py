@@ -17,6 +17,8 @@ Reported (one JSON line on stdout):
                per launch / its mean duration from HIP events on its stream,
                against 8 TB/s
   cpu_baseline the float64 oracle timed on a bounded sample on the host
+  mla, i8      side legs (not the headline): latent (MLA) attention, and the
+               same Llama-3-shaped stack on an int8 cache (codes + row scales)
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -54,6 +56,7 @@ def parse():
     p.add_argument("--cpu-repeats", type=int, default=100)
     p.add_argument("--eager-only", action="store_true", help="skip the graph-replay leg")
     p.add_argument("--no-mla", action="store_true", help="skip the latent (MLA) leg")
+    p.add_argument("--no-i8", action="store_true", help="skip the int8-cache leg")
     p.add_argument("--mla-workgroups", type=int, default=0,
                    help="force the latent leg's persistent grid size (0 = device default)")
     p.add_argument("--workgroups", type=int, default=0,
@@ -240,6 +243,85 @@ def bench_mla(torch, steps, warmup, workgroups=0):
     return res
 
 
+class I8Workload:
+    """The Llama-3-8B-shaped stack on an int8 cache (the same rows, queries and
+    valid lengths as the bf16 workload, quantised at fill): 32 layers of
+    int8 codes plus float32 row scales, resident on the GPU."""
+
+    def __init__(self, torch, dev):
+        from static_kv_cache_amd import kvc, synthetic
+        cfg = synthetic.WORKLOADS["llama3_8b_gqa_i8"]
+        L, B, H, Hkv, D, S = (cfg["n_layers"], cfg["batch"], cfg["n_heads"], cfg["n_kv_heads"],
+                              cfg["head_dim"], cfg["max_context"])
+        self.L, self.B, self.H, self.Hkv, self.D, self.S = L, B, H, Hkv, D, S
+        self.cache = kvc.Cache(kvc.gqa_desc(L, B, H, Hkv, D, S, "i8"))
+        c = synthetic.gqa_layer(cfg, seed_offset=0)
+        k = kvc.to_device(c["k_fill"], dev)
+        v = kvc.to_device(c["v_fill"], dev)
+        for layer in range(L):
+            self.cache.prefill_fill(layer, k, v, 0)
+        del k, v
+        rng = np.random.default_rng(cfg["seed"] + 7)
+        self.q = [kvc.to_device(synthetic.draw(rng, (B, H, D), "bf16"), dev) for _ in range(L)]
+        self.kn = [kvc.to_device(synthetic.draw(rng, (B, Hkv, 1, D), "bf16"), dev) for _ in range(L)]
+        self.vn = [kvc.to_device(synthetic.draw(rng, (B, Hkv, 1, D), "bf16"), dev) for _ in range(L)]
+        self.out = [torch.empty((B, H, D), dtype=torch.bfloat16, device=dev) for _ in range(L)]
+        self.valid = kvc.to_device(c["valid_lens"], dev)
+        self.ci = kvc.to_device(c["cache_index"], dev)
+        self.sm_scale = c["sm_scale"]
+        self.sum_valid = int(c["valid_lens"].sum())
+        # per layer: codes (1 byte per element) and one float32 scale per K and V row
+        self.kv_bytes = self.sum_valid * 2 * Hkv * (D + 4)
+        torch.cuda.synchronize()
+        self.cache.check()
+
+    def decode(self, layer):
+        self.cache.decode_attn(layer, self.q[layer], self.out[layer], valid_lens=self.valid,
+                               cache_index=self.ci, sm_scale=self.sm_scale)
+
+    def layer_step(self, layer):
+        self.cache.append(layer, self.kn[layer], self.vn[layer], self.ci)
+        self.decode(layer)
+
+
+def bench_i8(torch, steps, warmup, bf16_decode_us):
+    """Decode attention on the int8 cache (kvc_decode_attn) and the layer step
+    (kvc_append, which quantises the new rows, then kvc_decode_attn), per layer,
+    from HIP events around bursts of back-to-back launches over the 32 layers."""
+    wl = I8Workload(torch, torch.device("cuda:0"))
+    L = wl.L
+
+    def burst(fn):
+        for _ in range(warmup):
+            for layer in range(L):
+                fn(layer)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        torch.cuda.synchronize()
+        for e0, e1 in evs:
+            e0.record()
+            for layer in range(L):
+                fn(layer)
+            e1.record()
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) / L for a, b in evs]))
+
+    dec_ms = burst(wl.decode)
+    step_ms = burst(wl.layer_step)
+    wl.cache.check()
+    gbs = wl.kv_bytes / (dec_ms * 1e-3) / 1e9
+    res = dict(workload="llama3_8b_gqa_i8", batch=wl.B, n_heads=wl.H, n_kv_heads=wl.Hkv, head_dim=wl.D,
+               max_context=wl.S, sum_valid_len=wl.sum_valid, kv_bytes_per_layer=wl.kv_bytes,
+               decode_us=round(dec_ms * 1e3, 3), kv_gbs=round(gbs, 2), hbm_peak_frac=round(gbs / HBM_PEAK_GBS, 4),
+               speedup_vs_bf16_decode=round(bf16_decode_us / (dec_ms * 1e3), 3),
+               step_us=round(step_ms * 1e3, 3), layer_steps_per_s=round(1.0 / (step_ms * 1e-3), 1),
+               decode_steps_per_s=round(1.0 / (step_ms * 1e-3 * L), 2),
+               step="kvc_append (quantise the new rows) + kvc_decode_attn, per layer")
+    log(f"bench: i8 decode {dec_ms * 1e3:.2f} us ({gbs:.1f} GB/s of codes and scales), "
+        f"step {step_ms * 1e3:.2f} us; bf16 decode {bf16_decode_us:.2f} us")
+    wl.cache.free()
+    return res
+
+
 def time_steps(torch, fn, steps):
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -377,6 +459,7 @@ def main():
     wg_forced = wl.cache.workgroups()[0]
     wl.cache.free()
     mla = None if args.no_mla else bench_mla(torch, max(5, args.steps // 2), 2, args.mla_workgroups)
+    i8 = None if args.no_i8 else bench_i8(torch, max(5, args.steps // 2), 2, decode_ms * 1e3)
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl, args.cpu_repeats)
     line = {
         "metric": METRIC,
@@ -405,6 +488,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "mla": mla,
+        "i8": i8,
     }
     print(json.dumps(line), flush=True)
 

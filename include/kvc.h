@@ -26,8 +26,10 @@
  *    is enqueued asynchronously on it; the caller keeps every argument alive
  *    until that work has run.
  *  - Element type: every tensor that holds cache-typed values (k, v, q, out,
- *    latent rows, MLA weights) has the cache's dtype. Nothing is converted
- *    silently; there is no per-call dtype argument.
+ *    latent rows, MLA weights) has the cache's dtype, except on an int8
+ *    cache (KVC_I8), whose rows are stored as int8 codes but every tensor
+ *    handed in or out is bf16. Nothing else is converted; there is no
+ *    per-call dtype argument.
  *  - Index arrays (`cache_index`, `valid_lens`) are int32 device arrays of
  *    length B. They stay on the device so a decode step has fixed pointers
  *    and launch shapes and can be captured in a HIP graph.
@@ -59,7 +61,16 @@ typedef enum {
   KVC_ERR_DEVICE_RANGE = 6   /* a device-side index was out of range (kvc_check) */
 } kvc_status;
 
-typedef enum { KVC_F32 = 0, KVC_BF16 = 1 } kvc_dtype;
+/* KVC_I8: "10.3 - KV cache implementation details", section 4.4 (the cache
+ * stored in lower precision, p_cache = 1). Each cached row of one kv head,
+ * of K and of V separately, is stored as head_dim int8 codes plus one
+ * float32 scale, quantised once when the row is written (fill or append):
+ *   amax = max_i |x_i|, scale = amax / 127,
+ *   code_i = round_half_even(x_i * (127 / amax)) clamped to [-127, 127],
+ * all in IEEE binary32 (a row of zeros: scale 0, codes 0). The row stands
+ * for code_i * scale, and attention runs on those values. Rows handed in,
+ * queries and outputs are bf16. GQA only, head_dim 64, 128 or 256. */
+typedef enum { KVC_F32 = 0, KVC_BF16 = 1, KVC_I8 = 2 } kvc_dtype;
 
 /* KVC_ATTN_GQA covers MHA (n_kv_heads == n_heads), GQA and MQA
  * (n_kv_heads == 1) with one code path; KVC_ATTN_MLA is the latent cache. */
@@ -70,6 +81,8 @@ typedef enum { KVC_ATTN_GQA = 0, KVC_ATTN_MLA = 1 } kvc_attn;
  *  GQA: n_heads % n_kv_heads == 0; head_dim in {32, 64, 128, 256};
  *       latent_dim = rope_dim = 0.
  *       Layout: [n_layers][2 (K, V)][batch][n_kv_heads][max_context][head_dim].
+ *       KVC_I8: the codes in that layout, followed by the scales
+ *       [n_layers][2 (K, V)][batch][n_kv_heads][max_context] (float32).
  *  MLA: n_kv_heads = 1; latent_dim = 512, rope_dim = 64, head_dim = 128
  *       (per-head width of q_nope and of the output), bf16 only;
  *       n_heads <= 16 or a multiple of 16.
@@ -98,7 +111,9 @@ typedef struct kvc_cache kvc_cache; /* opaque */
  *   GQA: 2 * n_layers * n_kv_heads * head_dim * max_context * batch * p;
  * section 4.3 (with the rotary key stored in the same row):
  *   MLA: n_layers * (latent_dim + rope_dim) * max_context * batch * p;
- * p = 4 (fp32) or 2 (bf16). Returns KVC_ERR_INVALID_ARG for a bad desc. */
+ * p = 4 (fp32), 2 (bf16) or 1 (int8, section 4.4), and for int8 the
+ * scales add 2 * n_layers * n_kv_heads * max_context * batch * 4.
+ * Returns KVC_ERR_INVALID_ARG for a bad desc. */
 kvc_status kvc_bytes(const kvc_desc* desc, uint64_t* physical);
 
 /* Allocate a cache once, at full capacity ("AR Static KV-Cache"). If
@@ -118,6 +133,11 @@ kvc_status kvc_free(kvc_cache* cache);
  * MLA *k = [B][S][latent_dim + rope_dim] rows and *v = NULL. Host only. */
 kvc_status kvc_layer_ptrs(const kvc_cache* cache, int32_t layer, void** k, void** v);
 
+/* Device pointers of one layer's row scales on an int8 cache:
+ * *k_scales, *v_scales = float32 [B][H_kv][S]. Other caches:
+ * KVC_ERR_INVALID_ARG. Host only. */
+kvc_status kvc_layer_scales(const kvc_cache* cache, int32_t layer, void** k_scales, void** v_scales);
+
 /* Logical bytes of the live prefixes given HOST valid lengths [B]:
  * the byte formula with max_context * batch replaced by sum_b n_b
  * ("KV Cache Optimization ...", "File map": totalBytes reports logical bytes,
@@ -130,7 +150,8 @@ kvc_status kvc_logical_bytes(const kvc_cache* cache, const int32_t* host_valid_l
  *  v must be NULL.
  * ("KV-Cache Mechanics", "AR Static KV-Cache": prefill fills the cache from
  * cache_index 0; "KV Cache Optimization ...", "File map": migrateToPreAlloc.)
- * Bit copy. start < 0, t < 1 or start + t > max_context -> KVC_ERR_CAPACITY. */
+ * Bit copy (int8 cache: bf16 rows in, each row quantised as for KVC_I8).
+ * start < 0, t < 1 or start + t > max_context -> KVC_ERR_CAPACITY. */
 kvc_status kvc_prefill_fill(kvc_cache* cache, int32_t layer, const void* k, const void* v,
                             int32_t start, int32_t t, void* stream);
 
@@ -142,6 +163,8 @@ kvc_status kvc_prefill_fill(kvc_cache* cache, int32_t layer, const void* k, cons
  *  cache_index: device int32 [B].
  * ("KV Cache Optimization ...", "#2 ... After": slice-assign at the valid
  * length; "10.3 ...", section 5 step 2: append k_t, v_t before attention.)
+ * On an int8 cache the bf16 rows are quantised as for KVC_I8 (codes and
+ * scales of those rows are written, nothing else).
  * A sequence with cache_index[b] < 0 or cache_index[b] + t_new > max_context
  * is skipped and raises the device-range flag. t_new < 1 -> INVALID_ARG. */
 kvc_status kvc_append(kvc_cache* cache, int32_t layer, const void* k_new, const void* v_new,
@@ -157,7 +180,9 @@ kvc_status kvc_append(kvc_cache* cache, int32_t layer, const void* k_new, const 
  *       out = latent output [B][H][latent_dim];
  *       out[b,h] = softmax(sm_scale * R[b,:n_b] q[b,h]) R[b,:n_b,:latent_dim],
  *       R = the cached rows (latent then rotary key).
- * Accumulation is fp32; out is rounded to the cache dtype (nearest-even).
+ *  int8 cache: q and out bf16; K and V are the rows' code * scale values.
+ * Accumulation is fp32; out is rounded to the cache dtype (nearest-even;
+ * bf16 for an int8 cache).
  * n_b == 0 gives out[b] = 0. n_b < 0 or n_b > max_context gives out[b] = 0
  * and raises the device-range flag. At least one of valid_lens and
  * cache_index must be non-NULL. sm_scale must be finite and > 0. */
@@ -175,7 +200,7 @@ kvc_status kvc_decode_attn(kvc_cache* cache, int32_t layer, const void* q, void*
  * v_new, and the kernel writes it into the cache in the same launch, so the
  * output bits equal those of the two calls. A sequence with cache_index[b]
  * outside [0, max_context) is skipped (no write, zero output) and raises the
- * device-range flag. Latent caches: KVC_ERR_UNSUPPORTED. */
+ * device-range flag. Latent and int8 caches: KVC_ERR_UNSUPPORTED. */
 kvc_status kvc_append_decode_attn(kvc_cache* cache, int32_t layer, const void* k_new, const void* v_new,
                                   const void* q, void* out, const int32_t* cache_index, float sm_scale,
                                   void* stream);

@@ -22,7 +22,9 @@ bool env_sync_check() {
   return s && s[0] == '1';
 }
 
-int elem_size(int dtype) { return dtype == KVC_F32 ? 4 : (dtype == KVC_BF16 ? 2 : 0); }
+// Bytes per stored element: fp32 4, bf16 2, int8 codes 1 ("10.3 - KV cache
+// implementation details", section 4.4: p_cache).
+int elem_size(int dtype) { return dtype == KVC_F32 ? 4 : (dtype == KVC_BF16 ? 2 : (dtype == KVC_I8 ? 1 : 0)); }
 
 bool valid_gqa_head_dim(int d) { return d == 32 || d == 64 || d == 128 || d == 256; }
 
@@ -39,6 +41,8 @@ kvc_status validate_desc(const kvc_desc* d) {
     if (d->n_kv_heads < 1 || d->n_heads % d->n_kv_heads != 0) return KVC_ERR_INVALID_ARG;
     if (d->latent_dim != 0 || d->rope_dim != 0) return KVC_ERR_INVALID_ARG;
     if (!valid_gqa_head_dim(d->head_dim)) return KVC_ERR_UNSUPPORTED;
+    // int8 rows: a lane takes head_dim / 4 codes of a row in 16-byte vectors
+    if (d->dtype == KVC_I8 && d->head_dim < 64) return KVC_ERR_UNSUPPORTED;
     if ((int64_t)d->max_context * d->head_dim * elem_size(d->dtype) >= (int64_t)1 << 30)
       return KVC_ERR_UNSUPPORTED;
     return KVC_OK;
@@ -76,6 +80,19 @@ kvc_status bytes_of(const kvc_desc* d, uint64_t* out) {
     factors[n++] = (uint64_t)d->max_context;
     factors[n++] = (uint64_t)d->batch;
     factors[n++] = p;
+    if (d->dtype == KVC_I8) {
+      // plus one float32 scale per cached row of K and of V
+      uint64_t rows = 1;
+      const uint64_t rf[4] = {2, (uint64_t)d->n_layers, (uint64_t)d->n_kv_heads * (uint64_t)d->max_context,
+                              (uint64_t)d->batch * 4};
+      for (int i = 0; i < 4; ++i)
+        if (!mul_u64(rows, rf[i], &rows)) return KVC_ERR_INVALID_ARG;
+      for (int i = 0; i < n; ++i)
+        if (!mul_u64(x, factors[i], &x)) return KVC_ERR_INVALID_ARG;
+      if (x > UINT64_MAX - rows) return KVC_ERR_INVALID_ARG;
+      *out = x + rows;
+      return KVC_OK;
+    }
   } else {
     // L * (d_c + d_R) * S * B * p
     factors[n++] = (uint64_t)d->n_layers;
@@ -141,6 +158,10 @@ kvc_status kvc_alloc(const kvc_desc* desc, void* external, kvc_cache** out) {
     c->row_elems = desc->head_dim;
     c->kv_bytes = (uint64_t)desc->batch * desc->n_kv_heads * desc->max_context * desc->head_dim * c->elem;
     c->layer_bytes = 2 * c->kv_bytes;
+    if (desc->dtype == KVC_I8) {
+      c->scale_kv_bytes = (uint64_t)desc->batch * desc->n_kv_heads * desc->max_context * sizeof(float);
+      c->scale_layer_bytes = 2 * c->scale_kv_bytes;
+    }
   } else {
     c->row_elems = desc->latent_dim + desc->rope_dim;
     c->kv_bytes = 0;
@@ -160,6 +181,7 @@ kvc_status kvc_alloc(const kvc_desc* desc, void* external, kvc_cache** out) {
     c->owns_base = ok;
     if (ok) ok = hipMemset(c->base, 0, bytes) == hipSuccess;
   }
+  if (ok && desc->dtype == KVC_I8) c->scales = c->base + (uint64_t)desc->n_layers * c->layer_bytes;
   if (ok) ok = hipMalloc((void**)&c->ws_acc, c->ws_entries * acc_width * sizeof(float)) == hipSuccess;
   if (ok) ok = hipMalloc((void**)&c->ws_ml, c->ws_entries * 2 * sizeof(float)) == hipSuccess;
   const uint64_t cnt_bytes = (uint64_t)desc->batch * desc->n_heads * sizeof(int32_t);
@@ -204,6 +226,14 @@ kvc_status kvc_layer_ptrs(const kvc_cache* c, int32_t layer, void** k, void** v)
   return KVC_OK;
 }
 
+kvc_status kvc_layer_scales(const kvc_cache* c, int32_t layer, void** k_scales, void** v_scales) {
+  if (!c || !k_scales || !v_scales || !layer_ok(c, layer) || c->d.dtype != KVC_I8) return KVC_ERR_INVALID_ARG;
+  uint8_t* l = c->scales + (uint64_t)layer * c->scale_layer_bytes;
+  *k_scales = l;
+  *v_scales = l + c->scale_kv_bytes;
+  return KVC_OK;
+}
+
 kvc_status kvc_logical_bytes(const kvc_cache* c, const int32_t* host_valid_lens, uint64_t* out) {
   if (!c || !host_valid_lens || !out) return KVC_ERR_INVALID_ARG;
   uint64_t total = 0;
@@ -211,9 +241,9 @@ kvc_status kvc_logical_bytes(const kvc_cache* c, const int32_t* host_valid_lens,
     if (host_valid_lens[b] < 0 || host_valid_lens[b] > c->d.max_context) return KVC_ERR_CAPACITY;
     total += (uint64_t)host_valid_lens[b];
   }
-  const uint64_t per_row = c->d.attn == KVC_ATTN_GQA
-                               ? 2ull * c->d.n_kv_heads * c->d.head_dim * c->elem
-                               : (uint64_t)c->row_elems * c->elem;
+  uint64_t per_row = c->d.attn == KVC_ATTN_GQA ? 2ull * c->d.n_kv_heads * c->d.head_dim * c->elem
+                                               : (uint64_t)c->row_elems * c->elem;
+  if (c->d.dtype == KVC_I8) per_row += 2ull * c->d.n_kv_heads * sizeof(float);  // the rows' scales
   *out = (uint64_t)c->d.n_layers * per_row * total;
   return KVC_OK;
 }
@@ -229,9 +259,17 @@ kvc_status kvc_prefill_fill(kvc_cache* c, int32_t layer, const void* k, const vo
   uint8_t* vl;
   kvc_layer_ptrs(c, layer, (void**)&kl, (void**)&vl);
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = kvc_launch_copy_rows(k, v, kl, vl, c->d.batch, gqa ? c->d.n_kv_heads : 1, t,
-                                      c->row_elems * c->elem, c->d.max_context, nullptr, start,
-                                      c->err_flag, s);
+  hipError_t e;
+  if (c->d.dtype == KVC_I8) {
+    float* ks;
+    float* vs;
+    kvc_layer_scales(c, layer, (void**)&ks, (void**)&vs);
+    e = kvc_launch_quant_rows(k, v, kl, vl, ks, vs, c->d.batch, c->d.n_kv_heads, t, c->d.head_dim,
+                              c->d.max_context, nullptr, start, c->err_flag, s);
+  } else {
+    e = kvc_launch_copy_rows(k, v, kl, vl, c->d.batch, gqa ? c->d.n_kv_heads : 1, t, c->row_elems * c->elem,
+                             c->d.max_context, nullptr, start, c->err_flag, s);
+  }
   return after_launch(c, e, s);
 }
 
@@ -246,9 +284,17 @@ kvc_status kvc_append(kvc_cache* c, int32_t layer, const void* k_new, const void
   uint8_t* vl;
   kvc_layer_ptrs(c, layer, (void**)&kl, (void**)&vl);
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = kvc_launch_copy_rows(k_new, v_new, kl, vl, c->d.batch, gqa ? c->d.n_kv_heads : 1,
-                                      t_new, c->row_elems * c->elem, c->d.max_context, cache_index, 0,
-                                      c->err_flag, s);
+  hipError_t e;
+  if (c->d.dtype == KVC_I8) {
+    float* ks;
+    float* vs;
+    kvc_layer_scales(c, layer, (void**)&ks, (void**)&vs);
+    e = kvc_launch_quant_rows(k_new, v_new, kl, vl, ks, vs, c->d.batch, c->d.n_kv_heads, t_new, c->d.head_dim,
+                              c->d.max_context, cache_index, 0, c->err_flag, s);
+  } else {
+    e = kvc_launch_copy_rows(k_new, v_new, kl, vl, c->d.batch, gqa ? c->d.n_kv_heads : 1, t_new,
+                             c->row_elems * c->elem, c->d.max_context, cache_index, 0, c->err_flag, s);
+  }
   return after_launch(c, e, s);
 }
 
@@ -263,7 +309,12 @@ kvc_status kvc_decode_attn(kvc_cache* c, int32_t layer, const void* q, void* out
   kvc_layer_ptrs(c, layer, &kl, &vl);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
-  if (c->d.attn == KVC_ATTN_GQA)
+  if (c->d.attn == KVC_ATTN_GQA && c->d.dtype == KVC_I8) {
+    float* ks;
+    float* vs;
+    kvc_layer_scales(c, layer, (void**)&ks, (void**)&vs);
+    e = kvc_launch_gqa_decode(c, kl, vl, q, out, valid_lens, cache_index, sm_scale, s, nullptr, nullptr, ks, vs);
+  } else if (c->d.attn == KVC_ATTN_GQA)
     e = kvc_launch_gqa_decode(c, kl, vl, q, out, valid_lens, cache_index, sm_scale, s);
   else
     e = kvc_launch_mla_attn(c, kl, q, out, valid_lens, cache_index, sm_scale, s);
@@ -274,7 +325,7 @@ kvc_status kvc_append_decode_attn(kvc_cache* c, int32_t layer, const void* k_new
                                   const void* q, void* out, const int32_t* cache_index, float sm_scale,
                                   void* stream) {
   if (!c || !k_new || !v_new || !q || !out || !cache_index || !layer_ok(c, layer)) return KVC_ERR_INVALID_ARG;
-  if (c->d.attn != KVC_ATTN_GQA) return KVC_ERR_UNSUPPORTED;
+  if (c->d.attn != KVC_ATTN_GQA || c->d.dtype == KVC_I8) return KVC_ERR_UNSUPPORTED;
   if (!(sm_scale > 0.0f) || sm_scale > 3.0e38f) return KVC_ERR_INVALID_ARG;
   void* kl;
   void* vl;

@@ -143,6 +143,9 @@ struct DecodeArgs {
   float* ws_ml;                // [slot][GC][2]
   int32_t* ws_cnt;             // [B * H_kv * chunks] arrival counters (self-resetting)
   int32_t* err_flag;
+  // int8 caches: the layer's row scales [B][H_kv][S] (null otherwise)
+  const float* k_scale;
+  const float* v_scale;
   // Fused append (null for plain decode): the new rows [B][H_kv][1][D]. Row
   // n_b - 1 = cache_index[b] of every segment is then taken from here, not
   // from the cache, and written into the cache by the piece that ends there.
@@ -689,6 +692,18 @@ struct MfmaPiece {
     }
 
     fused_write<uint16_t, D>(a, b, kvg, chunk, fresh);
+    combine(a, sm, o, m, l, b, h0, whole, slot);
+  }
+
+  // End of a piece: combine the waves' (o, m, l) and write the output (whole
+  // segment) or the partial of `slot`. Every thread of the workgroup calls it.
+  static __device__ __forceinline__ void combine(const DecodeArgs& a, Smem& sm, const f32x4_t (&o)[NB], float m,
+                                                 float l, int b, int h0, bool whole, long long slot) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int g = lane >> 4;
+    const int j = lane & 15;
+    const int gc = a.chunk_heads;
     // denominators: sum the lane shares of each head column
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
@@ -733,6 +748,193 @@ struct MfmaPiece {
       }
     }
     __syncthreads();  // shared memory is reused by the next piece
+  }
+};
+
+// 16 int8 codes (one 16-byte vector) -> 16 bf16 values, as two 8-element
+// vectors. Exact: |code| <= 127 needs 7 significant bits; the bf16 is the
+// upper half of the code's binary32 value.
+__device__ __forceinline__ void codes_to_bf16(const u32x4_t& w, u32x4_t& lo, u32x4_t& hi) {
+  uint32_t r[8];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t x = w[q];
+    const float f0 = (float)(int)(int8_t)(x & 0xFFu);
+    const float f1 = (float)(int)(int8_t)((x >> 8) & 0xFFu);
+    const float f2 = (float)(int)(int8_t)((x >> 16) & 0xFFu);
+    const float f3 = (float)(int)(int8_t)(x >> 24);
+    r[2 * q] = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+    r[2 * q + 1] = __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u);
+  }
+  lo = u32x4_t{r[0], r[1], r[2], r[3]};
+  hi = u32x4_t{r[4], r[5], r[6], r[7]};
+}
+
+// int8 pieces ("10.3 - KV cache implementation details", section 4.4): the
+// matrix-core piece over int8 codes with a float32 scale per row. K row r
+// stands for code * sk[r] and V row r for code * sv[r], so
+//   score_r = sk[r] * (codes_r . q)   and   o = sum_r (p_r sv[r]) codes_r,
+// with l = sum_r p_r. Lane (g, j) takes the A operand of q.k from row j's
+// codes [g D/4, (g+1) D/4) (16-byte vectors), converted to bf16 in registers
+// (exact), and the query's B operand uses the same assignment of dims to
+// (lane, step); a dot product does not depend on the order of its dims. The
+// score tile is scaled by the rows' K scales. V codes are converted the same
+// way and staged in LDS as bf16 for the transpose read, and each row's V
+// scale is folded into the bf16 P operand. Rows past the piece read as zero
+// codes with zero scales and are masked. Half the bytes of the bf16 piece
+// per row, plus 8 bytes of scales.
+template <int D>
+struct I8Piece {
+  using Base = MfmaPiece<D>;
+  using Elem = uint16_t;                      // q, out and partials as for bf16
+  static constexpr int kD = D;
+  static constexpr int kSlotHeads = Base::kSlotHeads;
+  static constexpr int KS = D / 32;           // q.k steps of 32 dims
+  static constexpr int NB = D / 16;           // p.v output column blocks
+  static constexpr int TR = 16;               // rows per tile
+  static constexpr int CPR = D / 16;          // 16-byte code vectors per row
+  static constexpr int KL = D / 64;           // K code vectors per lane per tile (D / 4 codes)
+  static constexpr int VL = TR * CPR / 64;    // V code vectors per lane per tile
+  static constexpr int VSTRIDE = Base::VSTRIDE;
+  static constexpr int NBUF = Base::NBUF;
+  static_assert(D >= 64 && D % 64 == 0 && VL >= 1, "int8 head_dim must be 64, 128 or 256");
+  using Smem = typename Base::Smem;
+
+  struct Tile {
+    u32x4_t k[KL];
+    u32x4_t v[VL];
+    f32x4_t sk, sv;  // scales of rows 4g .. 4g + 3 of the tile
+  };
+
+  static __device__ __forceinline__ void run(const DecodeArgs& a, Smem& sm, int b, int kvg, int chunk,
+                                             int r_begin, int r_end, int n, bool whole, long long slot) {
+    b = uniform(b);
+    kvg = uniform(kvg);
+    chunk = uniform(chunk);
+    r_begin = uniform(r_begin);
+    r_end = uniform(r_end);
+    (void)n;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int g = lane >> 4;
+    const int j = lane & 15;
+    const int gc = a.chunk_heads;
+    const int h0 = kvg * (a.n_heads / a.n_kv_heads) + chunk * gc;
+    const float scale_log2 = a.scale_log2;
+
+    bf16x8_t qb[KS];
+    f32x4_t o[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) o[nb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    float m = -INFINITY;
+    float l = 0.0f;
+
+    // resources spanning exactly rows [0, r_end) of the (sequence, kv head)
+    const size_t row0 = ((size_t)b * a.n_kv_heads + kvg) * (size_t)a.max_context;
+    const __amdgpu_buffer_rsrc_t kres = buffer_rsrc(reinterpret_cast<const int8_t*>(a.k) + row0 * D, r_end * D);
+    const __amdgpu_buffer_rsrc_t vres = buffer_rsrc(reinterpret_cast<const int8_t*>(a.v) + row0 * D, r_end * D);
+    const __amdgpu_buffer_rsrc_t ksres = buffer_rsrc(a.k_scale + row0, r_end * 4);
+    const __amdgpu_buffer_rsrc_t vsres = buffer_rsrc(a.v_scale + row0, r_end * 4);
+    const int koff = j * D + g * (D / 4);  // row j, this lane's quarter of the dims
+    const int voff = lane * 16;            // V tile as contiguous 16-byte vectors
+    unsigned char* vs = sm.u.v[wave];
+
+    auto load_tile = [&](int base, Tile& tl) {
+      const int kb = base * D + koff;
+#pragma unroll
+      for (int i = 0; i < KL; ++i) tl.k[i] = __builtin_amdgcn_raw_buffer_load_b128(kres, kb + 16 * i, 0, 0);
+      const int vb = base * D + voff;
+#pragma unroll
+      for (int i = 0; i < VL; ++i) tl.v[i] = __builtin_amdgcn_raw_buffer_load_b128(vres, vb + 1024 * i, 0, 0);
+      tl.sk = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ksres, (base + 4 * g) * 4, 0, 0));
+      tl.sv = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(vsres, (base + 4 * g) * 4, 0, 0));
+    };
+    auto use_tile = [&](int base, const Tile& tl) {
+      // V codes -> bf16, staged row-major in LDS
+#pragma unroll
+      for (int i = 0; i < VL; ++i) {
+        const int f = i * 64 + lane;
+        u32x4_t lo, hi;
+        codes_to_bf16(tl.v[i], lo, hi);
+        unsigned char* dst = vs + (f / CPR) * VSTRIDE + (f % CPR) * 32;
+        *reinterpret_cast<u32x4_t*>(dst) = lo;
+        *reinterpret_cast<u32x4_t*>(dst + 16) = hi;
+      }
+      // scores: codes . q on the matrix cores, then the rows' K scales
+      f32x4_t sc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int i = 0; i < KL; ++i) {
+        u32x4_t lo, hi;
+        codes_to_bf16(tl.k[i], lo, hi);
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, lo), qb[2 * i], sc, 0, 0, 0);
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, hi), qb[2 * i + 1], sc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) sc[t] *= tl.sk[t];
+      if (base + TR > r_end) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) sc[t] = (base + 4 * g + t < r_end) ? sc[t] : -INFINITY;
+      }
+      // online softmax with a lazily moved reference maximum (as the bf16 piece)
+      const float cand = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])) * scale_log2;
+      if (__builtin_amdgcn_ballot_w64(cand > m + kLazyMfma)) {
+        float mt = fmaxf(cand, __shfl_xor(cand, 16));
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        const float mn = fmaxf(m, mt);
+        const float c = __builtin_amdgcn_exp2f(m - ((mn == -INFINITY) ? 0.0f : mn));
+        l *= c;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float ct = __shfl(c, 4 * g + t);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) o[nb][t] *= ct;
+        }
+        m = mn;
+      }
+      const float nm = (m == -INFINITY) ? 0.0f : -m;
+      s16x4_t pa;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sc[t], scale_log2, nm));
+        l += p;
+        pa[t] = __builtin_bit_cast(short, (__bf16)(p * tl.sv[t]));
+      }
+      // p.v: B operand = V[base + 4g + t][16 nb + j] by one transpose read
+      const unsigned char* vrow = vs + (4 * g + (j >> 2)) * VSTRIDE + 8 * (j & 3);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const s16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4_t*)(vrow + 32 * nb));
+        o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, o[nb], 0, 0, 0);
+      }
+    };
+
+    // Ring of NBUF register tiles as in the bf16 piece: loads past r_end are
+    // unconditional (zeros), tiles past r_end are skipped.
+    const int stride = kWaves * TR;
+    int base = r_begin + wave * TR;
+    Tile buf[NBUF];
+#pragma unroll
+    for (int i = 0; i < NBUF - 1; ++i) load_tile(base + i * stride, buf[i]);
+    {
+      const bool real = j < gc;
+      const uint16_t* qh =
+          reinterpret_cast<const uint16_t*>(a.q) + ((size_t)b * a.n_heads + h0 + (real ? j : 0)) * D + g * (D / 4);
+#pragma unroll
+      for (int k = 0; k < KS; ++k) {
+        u32x4_t v = *reinterpret_cast<const u32x4_t*>(qh + 8 * k);
+        v = real ? v : u32x4_t{0u, 0u, 0u, 0u};
+        qb[k] = __builtin_bit_cast(bf16x8_t, v);
+      }
+    }
+    for (; base < r_end; base += NBUF * stride) {
+#pragma unroll
+      for (int i = 0; i < NBUF; ++i) {
+        load_tile(base + (i + NBUF - 1) * stride, buf[(i + NBUF - 1) % NBUF]);
+        if (base + i * stride < r_end) use_tile(base + i * stride, buf[i]);
+      }
+    }
+    Base::combine(a, sm, o, m, l, b, h0, whole, slot);
   }
 };
 
@@ -822,6 +1024,15 @@ hipError_t launch_bf16(const kvc_cache* c, const DecodeArgs& a, hipStream_t st) 
   return launch_piece<MfmaPiece<D>, uint16_t, D>(c, a, gc, st);
 }
 
+// int8: matrix-core piece over codes; chunks of at most 16 heads as bf16.
+template <int D>
+hipError_t launch_i8(const kvc_cache* c, const DecodeArgs& a, hipStream_t st) {
+  const int group = c->d.n_heads / c->d.n_kv_heads;
+  int gc = group <= 16 ? group : 16;
+  while (group % gc != 0) --gc;
+  return launch_piece<I8Piece<D>, uint16_t, D>(c, a, gc, st);
+}
+
 // fp32: VALU piece with GC heads per chunk.
 template <int D>
 hipError_t launch_f32(const kvc_cache* c, const DecodeArgs& a, hipStream_t st) {
@@ -837,7 +1048,8 @@ hipError_t launch_f32(const kvc_cache* c, const DecodeArgs& a, hipStream_t st) {
 hipError_t kvc_launch_gqa_decode(const kvc_cache* c, const void* k_layer, const void* v_layer,
                                  const void* q, void* out, const int32_t* valid_lens,
                                  const int32_t* cache_index, float sm_scale, hipStream_t stream,
-                                 const void* k_new, const void* v_new) {
+                                 const void* k_new, const void* v_new, const float* k_scale,
+                                 const float* v_scale) {
   if (c->d.batch > KVC_MAX_BATCH || (long long)c->d.batch * c->d.n_heads > 0x7fffffffLL)
     return hipErrorInvalidValue;
   DecodeArgs a;
@@ -861,6 +1073,17 @@ hipError_t kvc_launch_gqa_decode(const kvc_cache* c, const void* k_layer, const 
   a.err_flag = c->err_flag;
   a.k_new = k_new;
   a.v_new = v_new;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  if (c->d.dtype == KVC_I8) {
+    if (k_new || !k_scale || !v_scale) return hipErrorInvalidValue;
+    switch (c->d.head_dim) {
+      case 64: return launch_i8<64>(c, a, stream);
+      case 128: return launch_i8<128>(c, a, stream);
+      case 256: return launch_i8<256>(c, a, stream);
+    }
+    return hipErrorInvalidValue;
+  }
   const bool bf16 = c->d.dtype == KVC_BF16;
   switch (c->d.head_dim) {
     case 32: return bf16 ? launch_bf16<32>(c, a, stream) : launch_f32<32>(c, a, stream);

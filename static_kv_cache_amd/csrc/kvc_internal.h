@@ -20,10 +20,13 @@ struct kvc_cache {
   uint8_t* base;          // cache region (one allocation, lives until kvc_free)
   bool owns_base;
   uint64_t bytes;         // physical bytes of the region
-  int elem;               // bytes per element (4 fp32, 2 bf16)
+  int elem;               // bytes per stored element (4 fp32, 2 bf16, 1 int8)
   uint64_t layer_bytes;   // bytes per layer (K and V together for GQA)
   uint64_t kv_bytes;      // offset of V from K inside a layer (GQA)
   int row_elems;          // elements per cached row: head_dim (GQA) or d_c + d_R (MLA)
+  uint64_t scale_layer_bytes;  // int8: bytes of one layer's K and V scales (0 otherwise)
+  uint64_t scale_kv_bytes;     // int8: offset of the V scales from the K scales in a layer
+  uint8_t* scales;        // int8: [L][2][B][H_kv][S] float32 scales (after the codes), else NULL
 
   // fixed workspace (allocated once by kvc_alloc)
   int max_workgroups;     // num_cus * KVC_MAX_WG_PER_CU
@@ -49,13 +52,24 @@ hipError_t kvc_launch_copy_rows(const void* src_k, const void* src_v, uint8_t* d
                                 const int32_t* dev_start, int host_start, int32_t* err_flag,
                                 hipStream_t stream);
 
+// Quantising row copy into an int8 cache: as kvc_launch_copy_rows for bf16
+// source rows [B][H_kv][t][d] (d = head_dim), writing each row's int8 codes
+// to dst_k / dst_v ([B][H_kv][S][d]) and its float32 scale to ks / vs
+// ([B][H_kv][S]).
+hipError_t kvc_launch_quant_rows(const void* src_k, const void* src_v, uint8_t* dst_k, uint8_t* dst_v,
+                                 float* ks, float* vs, int batch, int n_kv_heads, int t, int head_dim,
+                                 int max_context, const int32_t* dev_start, int host_start,
+                                 int32_t* err_flag, hipStream_t stream);
+
 // Persistent split-context GQA decode (pieces merged in the same kernel).
 // With k_new / v_new (and valid_lens null) the launch also appends the new
-// row at cache_index and attends it from k_new / v_new.
+// row at cache_index and attends it from k_new / v_new (not for int8). On an
+// int8 cache k_scale / v_scale are the layer's row scales.
 hipError_t kvc_launch_gqa_decode(const kvc_cache* c, const void* k_layer, const void* v_layer,
                                  const void* q, void* out, const int32_t* valid_lens,
                                  const int32_t* cache_index, float sm_scale, hipStream_t stream,
-                                 const void* k_new = nullptr, const void* v_new = nullptr);
+                                 const void* k_new = nullptr, const void* v_new = nullptr,
+                                 const float* k_scale = nullptr, const float* v_scale = nullptr);
 
 // Latent (MLA) decode over absorbed queries q_abs [B][H][d_c + d_R] (bf16)
 // into out_lat [B][H][d_c] (bf16).

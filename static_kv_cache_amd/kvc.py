@@ -20,10 +20,10 @@ LIB_PATH = os.path.join(_PKG, "libkvc.so")
 
 KVC_OK, KVC_ERR_INVALID_ARG, KVC_ERR_CAPACITY, KVC_ERR_OOM = 0, 1, 2, 3
 KVC_ERR_DEVICE, KVC_ERR_UNSUPPORTED, KVC_ERR_DEVICE_RANGE = 4, 5, 6
-KVC_F32, KVC_BF16 = 0, 1
+KVC_F32, KVC_BF16, KVC_I8 = 0, 1, 2
 KVC_ATTN_GQA, KVC_ATTN_MLA = 0, 1
 
-_DTYPES = {"f32": KVC_F32, "bf16": KVC_BF16}
+_DTYPES = {"f32": KVC_F32, "bf16": KVC_BF16, "i8": KVC_I8}
 
 
 class Desc(ctypes.Structure):
@@ -49,6 +49,7 @@ _SIGS = {
     "kvc_alloc": [ctypes.POINTER(Desc), _p, ctypes.POINTER(_p)],
     "kvc_free": [_p],
     "kvc_layer_ptrs": [_p, _i32, ctypes.POINTER(_p), ctypes.POINTER(_p)],
+    "kvc_layer_scales": [_p, _i32, ctypes.POINTER(_p), ctypes.POINTER(_p)],
     "kvc_logical_bytes": [_p, _p, ctypes.POINTER(ctypes.c_uint64)],
     "kvc_prefill_fill": [_p, _i32, _p, _p, _i32, _i32, _p],
     "kvc_append": [_p, _i32, _p, _p, _p, _i32, _p],
@@ -115,8 +116,14 @@ def _torch():
 
 
 def torch_dtype(dtype):
+    """Storage element type of a cache dtype ("i8": the int8 codes)."""
     torch = _torch()
-    return {"f32": torch.float32, "bf16": torch.bfloat16}[dtype]
+    return {"f32": torch.float32, "bf16": torch.bfloat16, "i8": torch.int8}[dtype]
+
+
+def io_dtype(dtype):
+    """Type of the tensors handed to and from a cache of `dtype` (bf16 for an int8 cache)."""
+    return "bf16" if dtype == "i8" else dtype
 
 
 def to_device(a, device):
@@ -143,7 +150,8 @@ class Cache:
     def __init__(self, desc, external=None):
         torch = _torch()
         self.desc = desc
-        self.dtype = {KVC_F32: "f32", KVC_BF16: "bf16"}[desc.dtype]
+        self.dtype = {KVC_F32: "f32", KVC_BF16: "bf16", KVC_I8: "i8"}[desc.dtype]
+        self.io_dtype = io_dtype(self.dtype)
         self.device = torch.device("cuda", torch.cuda.current_device())
         self.nbytes = cache_bytes(desc)
         self._external = external
@@ -169,7 +177,7 @@ class Cache:
 
     def _check(self, t, shape, dtype=None, name="tensor"):
         torch = _torch()
-        want = torch_dtype(self.dtype) if dtype is None else dtype
+        want = torch_dtype(self.io_dtype) if dtype is None else dtype
         if t.device != self.device:
             raise ValueError(f"{name} must be on {self.device}, got {t.device}")
         if t.dtype != want:
@@ -212,6 +220,19 @@ class Cache:
                 continue
             t = torch.empty(shape, dtype=torch_dtype(self.dtype), device=self.device)
             _memcpy_d2d(t.data_ptr(), ptr, n * t.element_size(), self.device)
+            out.append(t)
+        return tuple(out)
+
+    def layer_scales(self, layer):
+        """Copies of one layer's row scales of an int8 cache: (K, V) float32 [B, H_kv, S]."""
+        torch = _torch()
+        d = self.desc
+        k, v = ctypes.c_void_p(), ctypes.c_void_p()
+        _call("kvc_layer_scales", self.handle, layer, ctypes.byref(k), ctypes.byref(v))
+        out = []
+        for ptr in (k.value, v.value):
+            t = torch.empty((d.batch, d.n_kv_heads, d.max_context), dtype=torch.float32, device=self.device)
+            _memcpy_d2d(t.data_ptr(), ptr, t.numel() * 4, self.device)
             out.append(t)
         return tuple(out)
 

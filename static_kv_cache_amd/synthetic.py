@@ -37,6 +37,10 @@ WORKLOADS = {
     "llama3_8b_gqa_bf16": dict(attn="gqa", dtype="bf16", n_layers=32, batch=16, n_heads=32,
                                n_kv_heads=8, head_dim=128, max_context=4096,
                                valid_lo=1024, valid_hi=4096, seed=2),
+    # the same shape on an int8 cache (rows, queries and new rows drawn as bf16)
+    "llama3_8b_gqa_i8": dict(attn="gqa", dtype="i8", n_layers=32, batch=16, n_heads=32,
+                             n_kv_heads=8, head_dim=128, max_context=4096,
+                             valid_lo=1024, valid_hi=4096, seed=2),
     # long context: cache sized for 80 layers, one layer-step at a time
     "longctx_gqa_bf16": dict(attn="gqa", dtype="bf16", n_layers=80, batch=1, n_heads=64,
                              n_kv_heads=8, head_dim=128, max_context=32768, seed=3),
@@ -97,7 +101,7 @@ def gqa_layer(cfg, seed_offset=0, fill_rows=None, rng=None):
         rng = np.random.default_rng(cfg["seed"] + 1000 * seed_offset)
     B, H, Hkv, D, S = (cfg["batch"], cfg["n_heads"], cfg["n_kv_heads"],
                        cfg["head_dim"], cfg["max_context"])
-    dt = cfg["dtype"]
+    dt = "bf16" if cfg["dtype"] == "i8" else cfg["dtype"]  # an int8 cache takes bf16 rows
     T = S if fill_rows is None else fill_rows
     valid = gqa_valid_lens(cfg, rng)
     out = dict(

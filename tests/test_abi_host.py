@@ -57,6 +57,18 @@ def test_kvc_bytes_matches_oracle(lib, shape):
     assert got == cb.kv_cache_bytes(L, Hkv, D, S, B, 4 if dt == "f32" else 2)
 
 
+@pytest.mark.parametrize("shape", [
+    (1, 2, 8, 2, 64, 100), (32, 16, 32, 8, 128, 4096), (2, 3, 16, 1, 256, 70),
+])
+def test_kvc_bytes_int8_matches_oracle(lib, shape):
+    """int8 cache: codes at p_cache = 1 (section 4.4) plus one float32 scale per K and V row."""
+    from oracle import quant
+    L, B, H, Hkv, D, S = shape
+    got = kvc.cache_bytes(kvc.gqa_desc(L, B, H, Hkv, D, S, "i8"))
+    assert got == quant.int8_cache_bytes(L, Hkv, D, S, B)
+    assert got == cb.kv_cache_bytes(L, Hkv, D, S, B, 1) + 2 * L * Hkv * S * B * 4
+
+
 def test_kvc_bytes_printed_examples(lib):
     assert kvc.cache_bytes(kvc.gqa_desc(80, 1, 64, 64, 128, 4096, "bf16")) == 10737418240
     assert kvc.cache_bytes(kvc.gqa_desc(32, 1, 32, 32, 128, 1024, "f32")) == 1073741824
@@ -95,7 +107,9 @@ def test_unsupported_head_dim_and_null(lib):
     kvc.mla_desc(1, 1, 16, 1 << 20),            # latent rows of one sequence >= 2^30 bytes
     kvc.gqa_desc(1, 1, 8, 8, 256, 1 << 21, "bf16"),   # one (sequence, kv head) block >= 2^30 bytes
     kvc.gqa_desc(1, 2048, 8, 8, 32, 1 << 20, "bf16"),  # row space of all sequences >= 2^31
-], ids=["mla_heads", "mla_rows", "gqa_block", "row_space"])
+    kvc.gqa_desc(1, 2, 8, 8, 32, 64, "i8"),            # int8 rows need head_dim >= 64
+    kvc.mla_desc(1, 2, 16, 64, dtype="i8"),            # int8 latent cache
+], ids=["mla_heads", "mla_rows", "gqa_block", "row_space", "i8_head_dim", "i8_latent"])
 def test_unsupported_sizes(lib, desc):
     out = ctypes.c_uint64(0)
     assert lib.kvc_bytes(ctypes.byref(desc), ctypes.byref(out)) == kvc.KVC_ERR_UNSUPPORTED
