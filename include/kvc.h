@@ -200,7 +200,9 @@ kvc_status kvc_decode_attn(kvc_cache* cache, int32_t layer, const void* q, void*
  * v_new, and the kernel writes it into the cache in the same launch, so the
  * output bits equal those of the two calls. A sequence with cache_index[b]
  * outside [0, max_context) is skipped (no write, zero output) and raises the
- * device-range flag. Latent and int8 caches: KVC_ERR_UNSUPPORTED. */
+ * device-range flag. On an int8 cache the new rows are quantised as by
+ * kvc_append (the same codes and scales), attended from those codes and
+ * written into the cache. Latent caches: KVC_ERR_UNSUPPORTED. */
 kvc_status kvc_append_decode_attn(kvc_cache* cache, int32_t layer, const void* k_new, const void* v_new,
                                   const void* q, void* out, const int32_t* cache_index, float sm_scale,
                                   void* stream);

@@ -325,13 +325,16 @@ kvc_status kvc_append_decode_attn(kvc_cache* c, int32_t layer, const void* k_new
                                   const void* q, void* out, const int32_t* cache_index, float sm_scale,
                                   void* stream) {
   if (!c || !k_new || !v_new || !q || !out || !cache_index || !layer_ok(c, layer)) return KVC_ERR_INVALID_ARG;
-  if (c->d.attn != KVC_ATTN_GQA || c->d.dtype == KVC_I8) return KVC_ERR_UNSUPPORTED;
+  if (c->d.attn != KVC_ATTN_GQA) return KVC_ERR_UNSUPPORTED;
   if (!(sm_scale > 0.0f) || sm_scale > 3.0e38f) return KVC_ERR_INVALID_ARG;
   void* kl;
   void* vl;
   kvc_layer_ptrs(c, layer, &kl, &vl);
+  float* ks = nullptr;
+  float* vs = nullptr;
+  if (c->d.dtype == KVC_I8) kvc_layer_scales(c, layer, (void**)&ks, (void**)&vs);
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = kvc_launch_gqa_decode(c, kl, vl, q, out, nullptr, cache_index, sm_scale, s, k_new, v_new);
+  hipError_t e = kvc_launch_gqa_decode(c, kl, vl, q, out, nullptr, cache_index, sm_scale, s, k_new, v_new, ks, vs);
   return after_launch(c, e, s);
 }
 

@@ -798,7 +798,10 @@ struct I8Piece {
   static constexpr int VSTRIDE = Base::VSTRIDE;
   static constexpr int NBUF = Base::NBUF;
   static_assert(D >= 64 && D % 64 == 0 && VL >= 1, "int8 head_dim must be 64, 128 or 256");
-  using Smem = typename Base::Smem;
+  struct Smem : Base::Smem {
+    __attribute__((aligned(16))) int8_t nq[2][D];  // fused append: the new K and V rows' codes
+    float ns[2];                                   // and their scales
+  };
 
   struct Tile {
     u32x4_t k[KL];
@@ -813,7 +816,6 @@ struct I8Piece {
     chunk = uniform(chunk);
     r_begin = uniform(r_begin);
     r_end = uniform(r_end);
-    (void)n;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int g = lane >> 4;
@@ -830,11 +832,21 @@ struct I8Piece {
     float l = 0.0f;
 
     // resources spanning exactly rows [0, r_end) of the (sequence, kv head)
+    // Fused append: the new row `fresh` lies outside the resources (its cache
+    // row is stale until this launch writes it) and is quantised here, with
+    // the append kernel's arithmetic, into shared memory; the lanes that hold
+    // it take it from there when the tile is used.
+    const int fresh = uniform(fused_row(a, r_end, n));
+    const int r_cache = fresh >= 0 ? fresh : r_end;
     const size_t row0 = ((size_t)b * a.n_kv_heads + kvg) * (size_t)a.max_context;
-    const __amdgpu_buffer_rsrc_t kres = buffer_rsrc(reinterpret_cast<const int8_t*>(a.k) + row0 * D, r_end * D);
-    const __amdgpu_buffer_rsrc_t vres = buffer_rsrc(reinterpret_cast<const int8_t*>(a.v) + row0 * D, r_end * D);
-    const __amdgpu_buffer_rsrc_t ksres = buffer_rsrc(a.k_scale + row0, r_end * 4);
-    const __amdgpu_buffer_rsrc_t vsres = buffer_rsrc(a.v_scale + row0, r_end * 4);
+    const __amdgpu_buffer_rsrc_t kres = buffer_rsrc(reinterpret_cast<const int8_t*>(a.k) + row0 * D, r_cache * D);
+    const __amdgpu_buffer_rsrc_t vres = buffer_rsrc(reinterpret_cast<const int8_t*>(a.v) + row0 * D, r_cache * D);
+    const __amdgpu_buffer_rsrc_t ksres = buffer_rsrc(a.k_scale + row0, r_cache * 4);
+    const __amdgpu_buffer_rsrc_t vsres = buffer_rsrc(a.v_scale + row0, r_cache * 4);
+    if (fresh >= 0) {
+      if (wave < 2) quantize_new_row(a, sm, b, kvg, wave);
+      __syncthreads();
+    }
     const int koff = j * D + g * (D / 4);  // row j, this lane's quarter of the dims
     const int voff = lane * 16;            // V tile as contiguous 16-byte vectors
     unsigned char* vs = sm.u.v[wave];
@@ -849,7 +861,27 @@ struct I8Piece {
       tl.sk = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ksres, (base + 4 * g) * 4, 0, 0));
       tl.sv = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(vsres, (base + 4 * g) * 4, 0, 0));
     };
-    auto use_tile = [&](int base, const Tile& tl) {
+    auto use_tile = [&](int base, const Tile& tile, auto patch_tag) {
+      constexpr bool kPatch = decltype(patch_tag)::value;  // the piece holds the new row
+      Tile tl = tile;
+      if (kPatch && fresh >= base && fresh < base + TR) {  // this tile holds the new row
+        if (base + j == fresh) {
+#pragma unroll
+          for (int i = 0; i < KL; ++i) tl.k[i] = *reinterpret_cast<const u32x4_t*>(sm.nq[0] + g * (D / 4) + 16 * i);
+        }
+#pragma unroll
+        for (int i = 0; i < VL; ++i) {
+          const int f = i * 64 + lane;
+          if (base + f / CPR == fresh) tl.v[i] = *reinterpret_cast<const u32x4_t*>(sm.nq[1] + (f % CPR) * 16);
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          if (base + 4 * g + t == fresh) {
+            tl.sk[t] = sm.ns[0];
+            tl.sv[t] = sm.ns[1];
+          }
+        }
+      }
       // V codes -> bf16, staged row-major in LDS
 #pragma unroll
       for (int i = 0; i < VL; ++i) {
@@ -927,14 +959,64 @@ struct I8Piece {
         qb[k] = __builtin_bit_cast(bf16x8_t, v);
       }
     }
-    for (; base < r_end; base += NBUF * stride) {
+    // the loop is instantiated twice so that only the piece holding the new
+    // row pays for the check
+    auto stream = [&](auto patch_tag) {
+      for (; base < r_end; base += NBUF * stride) {
 #pragma unroll
-      for (int i = 0; i < NBUF; ++i) {
-        load_tile(base + (i + NBUF - 1) * stride, buf[(i + NBUF - 1) % NBUF]);
-        if (base + i * stride < r_end) use_tile(base + i * stride, buf[i]);
+        for (int i = 0; i < NBUF; ++i) {
+          load_tile(base + (i + NBUF - 1) * stride, buf[(i + NBUF - 1) % NBUF]);
+          if (base + i * stride < r_end) use_tile(base + i * stride, buf[i], patch_tag);
+        }
       }
-    }
+    };
+    if (fresh >= 0) stream(std::integral_constant<bool, true>());
+    else stream(std::integral_constant<bool, false>());
+    if (fresh >= 0 && chunk == 0) write_new_row(a, sm, b, kvg, fresh);
     Base::combine(a, sm, o, m, l, b, h0, whole, slot);
+  }
+
+  // One wave quantises the new row of (b, g) from k_new (kv = 0) or v_new
+  // (kv = 1) exactly as the append kernel does: row maximum (exact in any
+  // order), 127 / amax and amax / 127 correctly rounded, codes
+  // rint(x * (127 / amax)) clamped to [-127, 127]; a zero row gives zeros.
+  static __device__ __forceinline__ void quantize_new_row(const DecodeArgs& a, Smem& sm, int b, int g, int kv) {
+    constexpr int EPL = D / 64;  // elements per lane
+    const int lane = threadIdx.x & 63;
+    const uint16_t* src = reinterpret_cast<const uint16_t*>(kv == 0 ? a.k_new : a.v_new) +
+                          ((size_t)b * a.n_kv_heads + g) * D + lane * EPL;
+    float x[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) x[e] = __uint_as_float((uint32_t)src[e] << 16);
+    float amax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) amax = fmaxf(amax, fabsf(x[e]));
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    const bool zero = amax == 0.0f;
+    const float inv = zero ? 0.0f : __fdiv_rn(127.0f, amax);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      float c = rintf(__fmul_rn(x[e], inv));
+      c = fminf(fmaxf(c, -127.0f), 127.0f);
+      sm.nq[kv][lane * EPL + e] = (int8_t)(int)c;
+    }
+    if (lane == 0) sm.ns[kv] = zero ? 0.0f : __fdiv_rn(amax, 127.0f);
+  }
+
+  // ... and writes it into the cache (codes and scales), after the tile loop.
+  static __device__ __forceinline__ void write_new_row(const DecodeArgs& a, Smem& sm, int b, int g, int fresh) {
+    const size_t row = ((size_t)b * a.n_kv_heads + g) * (size_t)a.max_context + fresh;
+    const int t = threadIdx.x;
+    if (t < 2 * (D / 16)) {
+      const int kv = t / (D / 16);
+      const int v = t - kv * (D / 16);
+      int8_t* dst = reinterpret_cast<int8_t*>(const_cast<void*>(kv == 0 ? a.k : a.v)) + row * D + 16 * v;
+      *reinterpret_cast<u32x4_t*>(dst) = *reinterpret_cast<const u32x4_t*>(sm.nq[kv] + 16 * v);
+    } else if (t < 2 * (D / 16) + 2) {
+      const int kv = t - 2 * (D / 16);
+      const_cast<float*>(kv == 0 ? a.k_scale : a.v_scale)[row] = sm.ns[kv];
+    }
   }
 };
 
@@ -1076,7 +1158,7 @@ hipError_t kvc_launch_gqa_decode(const kvc_cache* c, const void* k_layer, const 
   a.k_scale = k_scale;
   a.v_scale = v_scale;
   if (c->d.dtype == KVC_I8) {
-    if (k_new || !k_scale || !v_scale) return hipErrorInvalidValue;
+    if (!k_scale || !v_scale) return hipErrorInvalidValue;
     switch (c->d.head_dim) {
       case 64: return launch_i8<64>(c, a, stream);
       case 128: return launch_i8<128>(c, a, stream);

@@ -4,8 +4,9 @@
   a code in binary32 (amax / 127, x * (127 / amax) rounded half to even).
 * Decode attention matches the oracle's attention over the dequantised rows (code * scale, float64)
   within the bf16 bound of the parity tests (q, out and the P operand are bf16).
-* Rows past the valid length never matter; out-of-range appends are skipped and flagged; the fused
-  append-decode call is not offered for int8 caches.
+* Rows past the valid length never matter; out-of-range appends are skipped and flagged.
+* The fused append-decode call quantises the new rows in the kernel: its output bits, codes and
+  scales equal those of kvc_append followed by kvc_decode_attn.
 """
 
 import numpy as np
@@ -183,12 +184,89 @@ def test_append_then_decode_step_on_device():
     assert_same_as_ref(cache, 0, ref)
     want = oatt.decode_attention(case["q"], ref.keys(0), ref.values(0), ci + 1, case["sm_scale"])
     tol_check(to_f64(out), want, "bf16", "append then decode")
-    # the fused call is not offered for int8 caches
-    with pytest.raises(kvc.KvcError) as e:
-        cache.append_decode_attn(0, kvc.to_device(case["k_new"], dev), kvc.to_device(case["v_new"], dev),
-                                 kvc.to_device(case["q"], dev), out, kvc.to_device(ci, dev), case["sm_scale"])
-    assert e.value.status == kvc.KVC_ERR_UNSUPPORTED
     cache.free()
+
+
+def garbage_case(seed, B, H, Hkv, D, S, ci):
+    """Rows from each sequence's new row on hold large finite garbage (3e4): the new row must come
+    from k_new / v_new, and nothing past it may be attended."""
+    case = synthetic.random_gqa_case(seed, B, H, Hkv, D, S, "i8", valid_lens=np.maximum(np.asarray(ci) + 1, 1))
+    case["cache_index"] = np.asarray(ci, dtype=np.int32)
+    junk = synthetic.f32_to_bf16_bits(np.float32(3.0e4))
+    for b, c in enumerate(ci):
+        if 0 <= c < S:
+            case["k_fill"][b, :, c:] = junk
+            case["v_fill"][b, :, c:] = junk
+    return case
+
+
+def two_ways(dev, case, B, H, Hkv, D, S, workgroups=None):
+    """(fused out bits, its codes/scales, separate out bits, its codes/scales, statuses, fused out f64)."""
+    res = []
+    for fused in (True, False):
+        cache = kvc.Cache(kvc.gqa_desc(1, B, H, Hkv, D, S, "i8"))
+        if workgroups is not None:
+            cache.set_workgroups(workgroups)
+        cache.prefill_fill(0, kvc.to_device(case["k_fill"], dev), kvc.to_device(case["v_fill"], dev), 0)
+        kn, vn = kvc.to_device(case["k_new"], dev), kvc.to_device(case["v_new"], dev)
+        q, ci = kvc.to_device(case["q"], dev), kvc.to_device(case["cache_index"], dev)
+        out = torch.empty((B, H, D), dtype=torch.bfloat16, device=dev)
+        if fused:
+            cache.append_decode_attn(0, kn, vn, q, out, ci, case["sm_scale"])
+        else:
+            cache.append(0, kn, vn, ci)
+            cache.decode_attn(0, q, out, cache_index=ci, sm_scale=case["sm_scale"])
+        status = cache.check_status()
+        res.append((bits_of(out, "bf16"), codes_scales(cache, 0), status, to_f64(out)))
+        cache.free()
+    return res
+
+
+def same_codes(a, b):
+    return all(np.array_equal(x.view(np.uint8) if x.dtype == np.int8 else x.view(np.uint32),
+                              y.view(np.uint8) if y.dtype == np.int8 else y.view(np.uint32)) for x, y in zip(a, b))
+
+
+FUSED_SHAPES = [(3, 32, 8, 128, 600), (2, 64, 2, 128, 300), (4, 8, 8, 64, 130), (2, 16, 1, 256, 90)]
+
+
+@pytest.mark.parametrize("B,H,Hkv,D,S", FUSED_SHAPES)
+def test_fused_equals_append_then_decode(B, H, Hkv, D, S):
+    dev = device()
+    ci = [0, S - 1, S // 2, 16][:B]
+    say(f"i8 fused: B={B} H={H} Hkv={Hkv} D={D} S={S} ci={ci}")
+    case = garbage_case(S + D + H, B, H, Hkv, D, S, ci)
+    (fo, fc, fs, fout), (so, sc, ss, _) = two_ways(dev, case, B, H, Hkv, D, S)
+    assert fs == ss == kvc.KVC_OK
+    assert same_codes(fc, sc), "codes or scales differ from append + decode"
+    assert np.array_equal(fo, so), "output bits differ from append + decode"
+    ref = RefQuantCache(1, B, Hkv, S, D)
+    ref.fill(0, case["k_fill"], case["v_fill"], 0)
+    ref.append(0, case["k_new"], case["v_new"], case["cache_index"])
+    want = oatt.decode_attention(case["q"], ref.keys(0), ref.values(0), np.asarray(ci) + 1, case["sm_scale"])
+    tol_check(fout, want, "bf16", "i8 fused")
+
+
+@pytest.mark.parametrize("workgroups", [1, 7, 333])
+def test_fused_grid_invariance(workgroups):
+    dev = device()
+    B, H, Hkv, D, S = 3, 16, 4, 128, 1000
+    case = garbage_case(91, B, H, Hkv, D, S, [999, 332, 16])
+    say(f"i8 fused workgroups={workgroups}")
+    (fo, fc, _, _), (so, sc, _, _) = two_ways(dev, case, B, H, Hkv, D, S, workgroups)
+    assert np.array_equal(fo, so) and same_codes(fc, sc)
+
+
+def test_fused_out_of_range_is_skipped_and_flagged():
+    dev = device()
+    B, H, Hkv, D, S = 3, 8, 2, 64, 50
+    case = synthetic.random_gqa_case(92, B, H, Hkv, D, S, "i8", valid_lens=[10, 1, 1])
+    case["cache_index"] = np.array([9, -1, S], dtype=np.int32)
+    (fo, fc, fs, fout), (so, sc, ss, _) = two_ways(dev, case, B, H, Hkv, D, S)
+    assert fs == kvc.KVC_ERR_DEVICE_RANGE
+    assert same_codes(fc, sc), "skipped sequences must be left untouched"
+    assert not fout[1:].any(), "skipped sequences give zeros"
+    assert np.array_equal(fo[0], so[0])
 
 
 def test_llama3_8b_shape_full_size():
