@@ -94,6 +94,25 @@ def causal_attention_nocache(q_seq, k_seq, v_seq, sm_scale):
     return out
 
 
+def prefill_attention(q, k_cache, v_cache, start, sm_scale):
+    """Causal attention of t new queries over a cache that already holds their rows.
+
+    "KV-Cache Mechanics", "AR Static KV-Cache": the prompt's forward pass fills
+    the cache from cache_index 0 (a later chunk continues at cache_index =
+    start); "10.3 - KV cache implementation details", section 3: query i of
+    the chunk (position start + i) attends positions 0 .. start + i.
+    q: [B, H, t, D]; k_cache, v_cache: [B, H_kv, S, D] holding rows
+    [0, start + t). Each query is the decode of that position with valid
+    length start + i + 1. Returns float64 [B, H, t, D].
+    """
+    q = widen(q)
+    B, H, t, D = q.shape
+    out = np.zeros((B, H, t, D), dtype=np.float64)
+    for i in range(t):
+        out[:, :, i] = decode_attention(q[:, :, i], k_cache, v_cache, np.full(B, start + i + 1), sm_scale)
+    return out
+
+
 def repeat_kv_heads(x, group):
     """[B, H_kv, S, D] -> [B, H_kv * group, S, D], each key/value head repeated
     ``group`` times contiguously (GQA written as MHA)."""

@@ -100,3 +100,25 @@ def test_brute_force_tiny():
         z = sum(w)
         for d in range(D):
             assert abs(o[0, h, d] - sum(w[j] * v[0, 0, j, d] for j in range(3)) / z) < 1e-12
+
+
+def test_prefill_attention_equals_nocache_causal():
+    """Prefill of a chunk [start, start + t) equals the last t rows of the no-cache causal attention
+    over the whole sequence (growing lists, no buffer); start = 0 is the plain prompt. Also against
+    torch's causal SDPA in float64 for start = 0."""
+    rng = np.random.default_rng(31)
+    B, H, Hkv, D, S = 2, 4, 2, 8, 12
+    k = rng.standard_normal((B, Hkv, S, D))
+    v = rng.standard_normal((B, Hkv, S, D))
+    q = rng.standard_normal((B, H, S, D))
+    for start, t in ((0, 7), (5, 7), (11, 1)):
+        got = att.prefill_attention(q[:, :, start:start + t], k, v, start, 0.3)
+        for b in range(B):
+            full = att.causal_attention_nocache(q[b].transpose(1, 0, 2), k[b].transpose(1, 0, 2),
+                                                v[b].transpose(1, 0, 2), 0.3)   # [S, H, D]
+            want = full[start:start + t].transpose(1, 0, 2)
+            assert np.allclose(got[b], want, rtol=0, atol=1e-12)
+    sd = F.scaled_dot_product_attention(torch.from_numpy(q[:, :, :7]), torch.from_numpy(att.repeat_kv_heads(k[:, :, :7], 2)),
+                                        torch.from_numpy(att.repeat_kv_heads(v[:, :, :7], 2)), is_causal=True,
+                                        scale=0.3).numpy()
+    assert np.allclose(att.prefill_attention(q[:, :, :7], k, v, 0, 0.3), sd, rtol=0, atol=1e-12)
