@@ -17,8 +17,9 @@ Reported (one JSON line on stdout):
                per launch / its mean duration from HIP events on its stream,
                against 8 TB/s
   cpu_baseline the float64 oracle timed on a bounded sample on the host
-  mla, i8      side legs (not the headline): latent (MLA) attention, and the
-               same Llama-3-shaped stack on an int8 cache (codes + row scales)
+  mla, i8,     side legs (not the headline): latent (MLA) attention, the same
+  prefill      Llama-3-shaped stack on an int8 cache (codes + row scales), and
+               the causal prefill of one 4096-token prompt
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -57,6 +58,7 @@ def parse():
     p.add_argument("--eager-only", action="store_true", help="skip the graph-replay leg")
     p.add_argument("--no-mla", action="store_true", help="skip the latent (MLA) leg")
     p.add_argument("--no-i8", action="store_true", help="skip the int8-cache leg")
+    p.add_argument("--no-prefill", action="store_true", help="skip the prefill leg")
     p.add_argument("--mla-workgroups", type=int, default=0,
                    help="force the latent leg's persistent grid size (0 = device default)")
     p.add_argument("--workgroups", type=int, default=0,
@@ -330,6 +332,50 @@ def bench_i8(torch, steps, warmup, bf16_decode_us):
     return res
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def bench_prefill(torch, steps, warmup):
+    """Prefill of one Llama-3-8B-shaped prompt (B=1, H=32, H_kv=8, d_h=128, 4096 tokens, bf16):
+    kvc_prefill_attn writes the rows into the cache and runs the causal attention, per layer.
+    FLOPs are the causal q.k and p.v products: 2 * 2 * H * d_h * sum_i (i + 1)."""
+    from static_kv_cache_amd import kvc, synthetic
+    dev = torch.device("cuda:0")
+    B, H, Hkv, D, T, L = 1, 32, 8, 128, 4096, 4
+    cache = kvc.Cache(kvc.gqa_desc(L, B, H, Hkv, D, T, "bf16"))
+    rng = np.random.default_rng(11)
+    q = kvc.to_device(synthetic.draw(rng, (B, H, T, D), "bf16"), dev)
+    k = kvc.to_device(synthetic.draw(rng, (B, Hkv, T, D), "bf16"), dev)
+    v = kvc.to_device(synthetic.draw(rng, (B, Hkv, T, D), "bf16"), dev)
+    out = torch.empty((B, H, T, D), dtype=torch.bfloat16, device=dev)
+    scale = 1.0 / math.sqrt(D)
+
+    def run():
+        for layer in range(L):
+            cache.prefill_attn(layer, q, k, v, out, 0, scale)
+
+    for _ in range(warmup):
+        run()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for e0, e1 in evs:
+        e0.record()
+        run()
+        e1.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) / L for a, b in evs]))
+    cache.check()
+    cache.free()
+    flops = 2 * 2 * H * D * (T * (T + 1) // 2) * B
+    tf = flops / (ms * 1e-3) / 1e12
+    log(f"bench: prefill {T} tokens, one layer {ms * 1e3:.1f} us ({tf:.1f} TFLOP/s causal)")
+    return dict(workload="llama3_8b_prompt4096_bf16", batch=B, n_heads=H, n_kv_heads=Hkv, head_dim=D, tokens=T,
+                layer_us=round(ms * 1e3, 2), flops_per_layer=flops, tflops=round(tf, 2),
+                mfma_peak_frac=round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                ttft_attention_ms_32_layers=round(ms * 32, 3),
+                step="kvc_prefill_attn: write the prompt rows into the cache + causal attention, per layer")
+
+
 def time_steps(torch, fn, steps):
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -468,6 +514,7 @@ def main():
     wl.cache.free()
     mla = None if args.no_mla else bench_mla(torch, max(5, args.steps // 2), 2, args.mla_workgroups)
     i8 = None if args.no_i8 else bench_i8(torch, max(5, args.steps // 2), 2, decode_ms * 1e3)
+    prefill = None if args.no_prefill else bench_prefill(torch, max(3, args.steps // 10), 1)
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl, args.cpu_repeats)
     line = {
         "metric": METRIC,
@@ -497,6 +544,7 @@ def main():
         "cpu_baseline": cpu,
         "mla": mla,
         "i8": i8,
+        "prefill": prefill,
     }
     print(json.dumps(line), flush=True)
 

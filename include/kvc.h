@@ -190,6 +190,21 @@ kvc_status kvc_decode_attn(kvc_cache* cache, int32_t layer, const void* q, void*
                            const int32_t* valid_lens, const int32_t* cache_index,
                            float sm_scale, void* stream);
 
+/* Prefill of a prompt chunk on one GQA layer ("KV-Cache Mechanics", "AR
+ * Static KV-Cache": the prompt's forward pass fills the cache from
+ * cache_index 0, and a later chunk continues at cache_index = start;
+ * "10.3 ...", section 3: causal attention; section 4.2: shared kv heads).
+ * Writes k, v = [B][H_kv][t][d_h] into rows [start, start + t) of every
+ * sequence (as kvc_prefill_fill), then computes the causal attention of the
+ * chunk's t queries q = [B][H][t][d_h] over the cache:
+ *   out[b,h,i] = softmax(sm_scale * K[b,g,0:start+i+1] q[b,h,i]) V[b,g,0:start+i+1],
+ *   g = h / (H / H_kv), out = [B][H][t][d_h]. Rows [0, start) must already
+ * hold the earlier part of the prompt. bf16 GQA caches only (others:
+ * KVC_ERR_UNSUPPORTED). start < 0 or start + t > max_context ->
+ * KVC_ERR_CAPACITY; t < 1 or a bad argument -> KVC_ERR_INVALID_ARG. */
+kvc_status kvc_prefill_attn(kvc_cache* cache, int32_t layer, const void* q, const void* k, const void* v,
+                            void* out, int32_t start, int32_t t, float sm_scale, void* stream);
+
 /* One decode step of one GQA layer in one launch: the same result as
  *   kvc_append(cache, layer, k_new, v_new, cache_index, 1, stream);
  *   kvc_decode_attn(cache, layer, q, out, NULL, cache_index, sm_scale, stream);

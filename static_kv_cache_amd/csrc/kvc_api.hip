@@ -321,6 +321,23 @@ kvc_status kvc_decode_attn(kvc_cache* c, int32_t layer, const void* q, void* out
   return after_launch(c, e, s);
 }
 
+kvc_status kvc_prefill_attn(kvc_cache* c, int32_t layer, const void* q, const void* k, const void* v, void* out,
+                            int32_t start, int32_t t, float sm_scale, void* stream) {
+  if (!c || !q || !k || !v || !out || !layer_ok(c, layer)) return KVC_ERR_INVALID_ARG;
+  if (c->d.attn != KVC_ATTN_GQA || c->d.dtype != KVC_BF16) return KVC_ERR_UNSUPPORTED;
+  if (t < 1) return KVC_ERR_INVALID_ARG;
+  if (start < 0 || (int64_t)start + t > c->d.max_context) return KVC_ERR_CAPACITY;
+  if (!(sm_scale > 0.0f) || sm_scale > 3.0e38f) return KVC_ERR_INVALID_ARG;
+  uint8_t* kl;
+  uint8_t* vl;
+  kvc_layer_ptrs(c, layer, (void**)&kl, (void**)&vl);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = kvc_launch_copy_rows(k, v, kl, vl, c->d.batch, c->d.n_kv_heads, t, c->row_elems * c->elem,
+                                      c->d.max_context, nullptr, start, c->err_flag, s);
+  if (e == hipSuccess) e = kvc_launch_prefill_attn(c, kl, vl, q, out, start, t, sm_scale, s);
+  return after_launch(c, e, s);
+}
+
 kvc_status kvc_append_decode_attn(kvc_cache* c, int32_t layer, const void* k_new, const void* v_new,
                                   const void* q, void* out, const int32_t* cache_index, float sm_scale,
                                   void* stream) {

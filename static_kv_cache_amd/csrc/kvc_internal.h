@@ -71,6 +71,11 @@ hipError_t kvc_launch_gqa_decode(const kvc_cache* c, const void* k_layer, const 
                                  const void* k_new = nullptr, const void* v_new = nullptr,
                                  const float* k_scale = nullptr, const float* v_scale = nullptr);
 
+// Causal prefill attention of a chunk [start, start + t) whose rows are
+// already in the cache (bf16 GQA): q, out = [B][H][t][D].
+hipError_t kvc_launch_prefill_attn(const kvc_cache* c, const void* k_layer, const void* v_layer, const void* q,
+                                   void* out, int start, int t, float sm_scale, hipStream_t stream);
+
 // Latent (MLA) decode over absorbed queries q_abs [B][H][d_c + d_R] (bf16)
 // into out_lat [B][H][d_c] (bf16).
 hipError_t kvc_launch_mla_attn(const kvc_cache* c, const void* rows_layer, const void* q_abs,

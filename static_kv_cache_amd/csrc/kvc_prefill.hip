@@ -1,0 +1,234 @@
+// Causal prefill attention over the static cache (bf16).
+//
+// What is computed ("KV-Cache Mechanics", "AR Static KV-Cache": the prompt's
+// forward pass fills the cache from cache_index 0, a later chunk continues
+// at cache_index = start; "10.3 - KV cache implementation details", section
+// 3, causal attention, and section 4.2 for shared key/value heads): after
+// the chunk's rows [start, start + t) are in the cache, query i of the chunk
+// (position start + i) of head h attends the cache rows 0 .. start + i of
+// kv head g = h / (H / H_kv):
+//     out[b,h,i] = softmax(sm_scale * K[b,g,0:start+i+1] q[b,h,i]) V[b,g,0:start+i+1].
+//
+// How (matrix cores, the decode piece's layout with query positions in
+// place of heads):
+//  - A workgroup of four waves takes hpw = min(G, 4) heads of one kv head
+//    (G = H / H_kv; 1 if G is not a power of two) and 64 / hpw positions;
+//    wave w takes head hpw0 + w % hpw and 16 positions. The K/V tiles of the
+//    kv head are therefore shared by all heads of the group the workgroup
+//    holds.
+//  - Keys go in tiles of 32 rows, staged row-major in LDS (skewed rows) by
+//    the whole workgroup, with the next tile in flight in registers.
+//  - Scores: S[key][query] on v_mfma_f32_16x16x32_bf16, 16 keys (A, from LDS)
+//    against the wave's 16 queries (B, in registers), per 16-key block.
+//    Causal mask per (key, query). fp32 online softmax in log2 units with a
+//    lazily moved reference maximum per query column.
+//  - p.v on v_mfma_f32_16x16x16_bf16 with V read back transposed from LDS by
+//    ds_read_b64_tr_b16; each wave keeps its own (o, m, l), so no cross-wave
+//    merge: the output rows are normalised and written by the wave.
+//  - Blocks whose keys all lie past a wave's last query are skipped by that
+//    wave; the query blocks with the most keys are launched first.
+
+#include "kvc_device.h"
+
+namespace {
+
+using namespace kvcd;
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kKeys = 32;                 // keys per tile
+constexpr float kLazy = 64.0f;            // log2 headroom before the reference maximum moves
+
+struct PrefillArgs {
+  const uint16_t* k;      // layer keys [B][H_kv][S][D]
+  const uint16_t* v;      // layer values
+  const uint16_t* q;      // [B][H][t][D]
+  uint16_t* out;          // [B][H][t][D]
+  float scale_log2;
+  int n_heads, n_kv_heads, max_context, start, t;
+  int hpw;                // heads per workgroup (1, 2 or 4)
+  int n_qblocks;          // position blocks of 64 / hpw per (b, head group)
+};
+
+template <int D>
+struct Prefill {
+  static constexpr int KS = D / 32;                 // q.k steps of 32 dims
+  static constexpr int NB = D / 16;                 // output column blocks
+  static constexpr int KSTRIDE = 2 * D + 16;        // bytes per staged K row
+  static constexpr int VSTRIDE = 2 * D + 32;        // bytes per staged V row
+  static constexpr int VEC = kKeys * 2 * D / 16 / kThreads;  // 16-byte vectors per thread per tile (K, and V)
+  static_assert(VEC >= 1 && kKeys * 2 * D % (16 * kThreads) == 0, "tile must split evenly");
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void prefill_attn_kernel(PrefillArgs a) {
+  using P = Prefill<D>;
+  __shared__ __attribute__((aligned(16))) unsigned char ks[kKeys * P::KSTRIDE];
+  __shared__ __attribute__((aligned(16))) unsigned char vsm[kKeys * P::VSTRIDE];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 4;
+  const int j = lane & 15;
+  const int hpw = a.hpw;
+  const int span = 64 / hpw;                        // positions per workgroup
+  const int qb = a.n_qblocks - 1 - (int)blockIdx.x; // most keys first
+  const int groups = a.n_heads / hpw;
+  const int b = (int)blockIdx.y / groups;
+  const int hg = (int)blockIdx.y - b * groups;
+  const int h = uniform(hg * hpw + wave % hpw);
+  const int p0 = uniform(qb * span + 16 * (wave / hpw));  // wave's first position in the chunk
+  const int kvh = (hg * hpw) / (a.n_heads / a.n_kv_heads);
+  const int last = min(qb * span + span, a.t) - 1;  // last position of the workgroup
+  const int kend = a.start + last + 1;              // keys [0, kend) are needed
+  const int wave_kend = a.start + min(p0 + 15, a.t - 1) + 1;  // this wave's keys
+
+  // the kv head's rows [0, start + t) as resources (loads past them read zeros)
+  const size_t row0 = ((size_t)b * a.n_kv_heads + kvh) * (size_t)a.max_context;
+  const int rows = a.start + a.t;
+  const __amdgpu_buffer_rsrc_t kres = buffer_rsrc(a.k + row0 * D, rows * (2 * D));
+  const __amdgpu_buffer_rsrc_t vres = buffer_rsrc(a.v + row0 * D, rows * (2 * D));
+
+  // the wave's 16 queries as the B operand: column j is position p0 + j
+  bf16x8_t qb_[P::KS];
+  {
+    const bool real = p0 + j < a.t;
+    const uint16_t* qh = a.q + (((size_t)b * a.n_heads + h) * a.t + (real ? p0 + j : 0)) * D + 8 * g;
+#pragma unroll
+    for (int k = 0; k < P::KS; ++k) {
+      u32x4_t x = *reinterpret_cast<const u32x4_t*>(qh + 32 * k);
+      x = real ? x : u32x4_t{0u, 0u, 0u, 0u};
+      qb_[k] = __builtin_bit_cast(bf16x8_t, x);
+    }
+  }
+
+  f32x4_t o[P::NB];
+#pragma unroll
+  for (int nb = 0; nb < P::NB; ++nb) o[nb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  float m = -INFINITY;
+  float l = 0.0f;
+  const float scale_log2 = a.scale_log2;
+  const int qpos = a.start + p0 + j;  // absolute position of this lane's query column
+
+  // tile staging: thread t moves 16-byte vectors t + 256 i of the K and V tiles
+  u32x4_t kr[P::VEC], vr[P::VEC];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < P::VEC; ++i) {
+      const int f = (int)threadIdx.x + i * kThreads;
+      kr[i] = __builtin_amdgcn_raw_buffer_load_b128(kres, k0 * (2 * D) + f * 16, 0, 0);
+      vr[i] = __builtin_amdgcn_raw_buffer_load_b128(vres, k0 * (2 * D) + f * 16, 0, 0);
+    }
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int i = 0; i < P::VEC; ++i) {
+      const int f = (int)threadIdx.x + i * kThreads;
+      const int r = f / (D / 8), c = f % (D / 8);
+      *reinterpret_cast<u32x4_t*>(ks + r * P::KSTRIDE + c * 16) = kr[i];
+      *reinterpret_cast<u32x4_t*>(vsm + r * P::VSTRIDE + c * 16) = vr[i];
+    }
+  };
+
+  load(0);
+  for (int k0 = 0; k0 < kend; k0 += kKeys) {
+    __syncthreads();  // every wave is done with the previous tile
+    stage();
+    if (k0 + kKeys < kend) load(k0 + kKeys);
+    __syncthreads();  // the tile is visible
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      const int kb0 = k0 + 16 * blk;
+      if (kb0 >= wave_kend) continue;  // all keys past this wave's queries
+      // scores of keys kb0 + 4g + u against query column j
+      const unsigned char* arow = ks + (16 * blk + j) * P::KSTRIDE + 16 * g;
+      bf16x8_t av[P::KS];
+#pragma unroll
+      for (int k = 0; k < P::KS; ++k) av[k] = *reinterpret_cast<const bf16x8_t*>(arow + 64 * k);
+      f32x4_t sc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int k = 0; k < P::KS; ++k) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[k], qb_[k], sc, 0, 0, 0);
+      if (kb0 + 15 > a.start + p0) {  // the block reaches past some query: causal mask
+#pragma unroll
+        for (int u = 0; u < 4; ++u) sc[u] = (kb0 + 4 * g + u <= qpos) ? sc[u] : -INFINITY;
+      }
+      const float cand = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])) * scale_log2;
+      if (__builtin_amdgcn_ballot_w64(cand > m + kLazy)) {
+        float mt = fmaxf(cand, __shfl_xor(cand, 16));
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        const float mn = fmaxf(m, mt);
+        const float c = __builtin_amdgcn_exp2f(m - ((mn == -INFINITY) ? 0.0f : mn));
+        l *= c;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float cu = __shfl(c, 4 * g + u);  // factor of output row (query) 4g + u
+#pragma unroll
+          for (int nb = 0; nb < P::NB; ++nb) o[nb][u] *= cu;
+        }
+        m = mn;
+      }
+      const float nm = (m == -INFINITY) ? 0.0f : -m;
+      s16x4_t pa;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sc[u], scale_log2, nm));
+        l += p;
+        pa[u] = __builtin_bit_cast(short, (__bf16)p);
+      }
+      // p.v: B operand = V[kb0 + 4g + u][16 nb + j] by one transpose read
+      const unsigned char* vrow = vsm + (16 * blk + 4 * g + (j >> 2)) * P::VSTRIDE + 8 * (j & 3);
+#pragma unroll
+      for (int nb = 0; nb < P::NB; ++nb) {
+        const s16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4_t*)(vrow + 32 * nb));
+        o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, o[nb], 0, 0, 0);
+      }
+    }
+  }
+
+  // normalise and write: lane (g, j) holds output rows (queries) 4g + u, columns 16 nb + j
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int qi = p0 + 4 * g + u;
+    const float lr = __shfl(l, 4 * g + u);
+    if (qi < a.t) {
+      uint16_t* dst = a.out + (((size_t)b * a.n_heads + h) * a.t + qi) * D + j;
+      const float inv = 1.0f / lr;  // lr >= 1: the query attends at least its own key
+#pragma unroll
+      for (int nb = 0; nb < P::NB; ++nb) dst[16 * nb] = bf16_rne(o[nb][u] * inv);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t kvc_launch_prefill_attn(const kvc_cache* c, const void* k_layer, const void* v_layer, const void* q,
+                                   void* out, int start, int t, float sm_scale, hipStream_t stream) {
+  PrefillArgs a;
+  a.k = static_cast<const uint16_t*>(k_layer);
+  a.v = static_cast<const uint16_t*>(v_layer);
+  a.q = static_cast<const uint16_t*>(q);
+  a.out = static_cast<uint16_t*>(out);
+  a.scale_log2 = sm_scale * kLog2e;
+  a.n_heads = c->d.n_heads;
+  a.n_kv_heads = c->d.n_kv_heads;
+  a.max_context = c->d.max_context;
+  a.start = start;
+  a.t = t;
+  const int G = a.n_heads / a.n_kv_heads;
+  a.hpw = G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1);
+  const int span = 64 / a.hpw;
+  a.n_qblocks = (t + span - 1) / span;
+  const long long ny = (long long)c->d.batch * (a.n_heads / a.hpw);
+  if (ny > 65535 || a.n_qblocks > 0x7fffffff) return hipErrorInvalidValue;
+  dim3 grid((unsigned)a.n_qblocks, (unsigned)ny);
+  switch (c->d.head_dim) {
+    case 64: prefill_attn_kernel<64><<<grid, dim3(kThreads), 0, stream>>>(a); break;
+    case 128: prefill_attn_kernel<128><<<grid, dim3(kThreads), 0, stream>>>(a); break;
+    case 256: prefill_attn_kernel<256><<<grid, dim3(kThreads), 0, stream>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}

@@ -56,6 +56,7 @@ _SIGS = {
     "kvc_decode_attn": [_p, _i32, _p, _p, _p, _p, ctypes.c_float, _p],
     "kvc_mla_decode": [_p, _i32, _p, _p, _p, _p, _p, _p, _p, ctypes.c_float, _p],
     "kvc_append_decode_attn": [_p, _i32, _p, _p, _p, _p, _p, ctypes.c_float, _p],
+    "kvc_prefill_attn": [_p, _i32, _p, _p, _p, _p, _i32, _i32, ctypes.c_float, _p],
     "kvc_set_workgroups": [_p, _i32],
     "kvc_get_workgroups": [_p, ctypes.POINTER(_i32), ctypes.POINTER(_i32)],
     "kvc_check": [_p, _p],
@@ -296,6 +297,18 @@ class Cache:
         op = self._check(out, (d.batch, d.n_heads, d.head_dim), name="out")
         _call("kvc_append_decode_attn", self.handle, layer, kp, vp, qp, op, self._idx(cache_index, "cache_index"),
               float(sm_scale), _stream(self.device))
+
+    def prefill_attn(self, layer, q, k, v, out, start, sm_scale):
+        """Write the chunk's rows [start, start + t) and compute its causal attention
+        (kvc_prefill_attn): q, out [B, H, t, D]; k, v [B, H_kv, t, D]."""
+        d = self.desc
+        t = q.shape[2]
+        qp = self._check(q, (d.batch, d.n_heads, t, d.head_dim), name="q")
+        op = self._check(out, (d.batch, d.n_heads, t, d.head_dim), name="out")
+        shape = (d.batch, d.n_kv_heads, t, d.head_dim)
+        kp, vp = self._check(k, shape, name="k"), self._check(v, shape, name="v")
+        _call("kvc_prefill_attn", self.handle, layer, qp, kp, vp, op, start, t, float(sm_scale),
+              _stream(self.device))
 
     def mla_decode(self, layer, q_nope, q_rope, w_uk, w_uv, out, valid_lens=None, cache_index=None,
                    sm_scale=None):
