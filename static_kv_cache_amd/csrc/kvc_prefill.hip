@@ -30,7 +30,8 @@
 //    ds_read_b64_tr_b16; each wave keeps its own (o, m, l), so no cross-wave
 //    merge: the output rows are normalised and written by the wave.
 //  - Blocks whose keys all lie past a wave's last query are skipped by that
-//    wave; the query blocks with the most keys are launched first.
+//    wave; the query blocks with the most keys are launched first, for every
+//    head group.
 
 #include "kvc_device.h"
 
@@ -82,10 +83,12 @@ __global__ __launch_bounds__(kThreads) void prefill_attn_kernel(PrefillArgs a) {
   const int j = lane & 15;
   const int hpw = a.hpw;
   const int span = 64 * QG / hpw;                   // positions per workgroup
-  const int qb = a.n_qblocks - 1 - (int)blockIdx.x; // most keys first
+  // x (dispatched fastest) runs over (sequence, head group), y over position
+  // blocks with the most keys first, so every head group's heavy blocks go first
+  const int qb = a.n_qblocks - 1 - (int)blockIdx.y;
   const int groups = a.n_heads / hpw;
-  const int b = (int)blockIdx.y / groups;
-  const int hg = (int)blockIdx.y - b * groups;
+  const int b = (int)blockIdx.x / groups;
+  const int hg = (int)blockIdx.x - b * groups;
   const int h = uniform(hg * hpw + wave % hpw);
   const int p0 = uniform(qb * span + 16 * QG * (wave / hpw));  // wave's first position; group qg adds 16 qg
   const int kvh = (hg * hpw) / (a.n_heads / a.n_kv_heads);
@@ -258,9 +261,9 @@ hipError_t kvc_launch_prefill_attn(const kvc_cache* c, const void* k_layer, cons
   constexpr int QG = KVC_PREFILL_QG;
   const int span = 64 * QG / a.hpw;
   a.n_qblocks = (t + span - 1) / span;
-  const long long ny = (long long)c->d.batch * (a.n_heads / a.hpw);
-  if (ny > 65535 || a.n_qblocks > 0x7fffffff) return hipErrorInvalidValue;
-  dim3 grid((unsigned)a.n_qblocks, (unsigned)ny);
+  const long long nx = (long long)c->d.batch * (a.n_heads / a.hpw);
+  if (nx > 0x7fffffff || a.n_qblocks > 65535) return hipErrorInvalidValue;
+  dim3 grid((unsigned)nx, (unsigned)a.n_qblocks);
   switch (c->d.head_dim) {
     case 64: prefill_attn_kernel<64, QG><<<grid, dim3(kThreads), 0, stream>>>(a); break;
     case 128: prefill_attn_kernel<128, QG><<<grid, dim3(kThreads), 0, stream>>>(a); break;
