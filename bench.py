@@ -18,8 +18,9 @@ Reported (one JSON line on stdout):
                against 8 TB/s
   cpu_baseline the float64 oracle timed on a bounded sample on the host
   mla, i8,     side legs (not the headline): latent (MLA) attention, the same
-  prefill      Llama-3-shaped stack on an int8 cache (codes + row scales), and
-               the causal prefill of one 4096-token prompt
+  prefill,     Llama-3-shaped stack on an int8 cache (codes + row scales), the
+  paged        causal prefill of one 4096-token prompt, and the same stack on a
+               block-table cache of 16-row blocks scattered over the pool
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -59,6 +60,7 @@ def parse():
     p.add_argument("--no-mla", action="store_true", help="skip the latent (MLA) leg")
     p.add_argument("--no-i8", action="store_true", help="skip the int8-cache leg")
     p.add_argument("--no-prefill", action="store_true", help="skip the prefill leg")
+    p.add_argument("--no-paged", action="store_true", help="skip the block-table cache leg")
     p.add_argument("--mla-workgroups", type=int, default=0,
                    help="force the latent leg's persistent grid size (0 = device default)")
     p.add_argument("--workgroups", type=int, default=0,
@@ -332,6 +334,91 @@ def bench_i8(torch, steps, warmup, bf16_decode_us):
     return res
 
 
+class PagedWorkload:
+    """The Llama-3-8B-shaped stack on a block-table cache: 32 layers of pools of
+    16-row blocks, each sequence's blocks scattered over the pool by a random
+    table, holding the same rows, queries and valid lengths as the static
+    workload."""
+
+    BLOCK = 16
+
+    def __init__(self, torch, dev):
+        from static_kv_cache_amd import kvc, synthetic
+        cfg = synthetic.WORKLOADS[WORKLOAD]
+        L, B, H, Hkv, D, S = (cfg["n_layers"], cfg["batch"], cfg["n_heads"], cfg["n_kv_heads"],
+                              cfg["head_dim"], cfg["max_context"])
+        self.L, self.B, self.H, self.Hkv, self.D, self.S = L, B, H, Hkv, D, S
+        W = S // self.BLOCK
+        self.num_blocks = B * W
+        self.cache = kvc.PagedCache(kvc.gqa_desc(L, B, H, Hkv, D, S, "bf16"), self.BLOCK, self.num_blocks)
+        rng = np.random.default_rng(cfg["seed"] + 13)
+        self.table = kvc.to_device(rng.permutation(self.num_blocks).reshape(B, W).astype(np.int32), dev)
+        c = synthetic.gqa_layer(cfg, seed_offset=0)
+        k = kvc.to_device(c["k_fill"], dev)
+        v = kvc.to_device(c["v_fill"], dev)
+        zero = kvc.to_device(np.zeros(B, dtype=np.int32), dev)
+        for layer in range(L):
+            self.cache.paged_append(layer, k, v, self.table, zero)
+        del k, v
+        self.q = [kvc.to_device(synthetic.draw(rng, (B, H, D), "bf16"), dev) for _ in range(L)]
+        self.kn = [kvc.to_device(synthetic.draw(rng, (B, Hkv, 1, D), "bf16"), dev) for _ in range(L)]
+        self.vn = [kvc.to_device(synthetic.draw(rng, (B, Hkv, 1, D), "bf16"), dev) for _ in range(L)]
+        self.out = [torch.empty((B, H, D), dtype=torch.bfloat16, device=dev) for _ in range(L)]
+        self.valid = kvc.to_device(c["valid_lens"], dev)
+        self.ci = kvc.to_device(c["cache_index"], dev)
+        self.sm_scale = c["sm_scale"]
+        self.sum_valid = int(c["valid_lens"].sum())
+        self.kv_bytes = self.sum_valid * 2 * Hkv * D * 2
+        torch.cuda.synchronize()
+        self.cache.check()
+
+    def decode(self, layer):
+        self.cache.paged_decode_attn(layer, self.q[layer], self.out[layer], self.table, valid_lens=self.valid,
+                                     cache_index=self.ci, sm_scale=self.sm_scale)
+
+    def layer_step(self, layer):
+        self.cache.paged_append(layer, self.kn[layer], self.vn[layer], self.table, self.ci)
+        self.decode(layer)
+
+
+def bench_paged(torch, steps, warmup, bf16_decode_us):
+    """Decode attention through block tables (kvc_paged_decode_attn) and the
+    layer step (kvc_paged_append + kvc_paged_decode_attn), per layer, from HIP
+    events around bursts of back-to-back launches over the 32 layers."""
+    wl = PagedWorkload(torch, torch.device("cuda:0"))
+    L = wl.L
+
+    def burst(fn):
+        for _ in range(warmup):
+            for layer in range(L):
+                fn(layer)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        torch.cuda.synchronize()
+        for e0, e1 in evs:
+            e0.record()
+            for layer in range(L):
+                fn(layer)
+            e1.record()
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) / L for a, b in evs]))
+
+    dec_ms = burst(wl.decode)
+    step_ms = burst(wl.layer_step)
+    wl.cache.check()
+    gbs = wl.kv_bytes / (dec_ms * 1e-3) / 1e9
+    res = dict(workload="llama3_8b_gqa_paged16", batch=wl.B, n_heads=wl.H, n_kv_heads=wl.Hkv, head_dim=wl.D,
+               max_context=wl.S, block_size=wl.BLOCK, num_blocks=wl.num_blocks, table="random permutation",
+               sum_valid_len=wl.sum_valid, kv_bytes_per_layer=wl.kv_bytes,
+               decode_us=round(dec_ms * 1e3, 3), kv_gbs=round(gbs, 2), hbm_peak_frac=round(gbs / HBM_PEAK_GBS, 4),
+               vs_static_decode=round(bf16_decode_us / (dec_ms * 1e3), 3),
+               step_us=round(step_ms * 1e3, 3), layer_steps_per_s=round(1.0 / (step_ms * 1e-3), 1),
+               step="kvc_paged_append + kvc_paged_decode_attn, per layer")
+    log(f"bench: paged decode {dec_ms * 1e3:.2f} us ({gbs:.1f} GB/s), step {step_ms * 1e3:.2f} us; "
+        f"static decode {bf16_decode_us:.2f} us")
+    wl.cache.free()
+    return res
+
+
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
@@ -515,6 +602,7 @@ def main():
     mla = None if args.no_mla else bench_mla(torch, max(5, args.steps // 2), 2, args.mla_workgroups)
     i8 = None if args.no_i8 else bench_i8(torch, max(5, args.steps // 2), 2, decode_ms * 1e3)
     prefill = None if args.no_prefill else bench_prefill(torch, max(3, args.steps // 10), 1)
+    paged = None if args.no_paged else bench_paged(torch, max(5, args.steps // 2), 2, decode_ms * 1e3)
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl, args.cpu_repeats)
     line = {
         "metric": METRIC,
@@ -545,6 +633,7 @@ def main():
         "mla": mla,
         "i8": i8,
         "prefill": prefill,
+        "paged": paged,
     }
     print(json.dumps(line), flush=True)
 

@@ -237,6 +237,54 @@ kvc_status kvc_mla_decode(kvc_cache* cache, int32_t layer, const void* q_nope, c
                           const int32_t* valid_lens, const int32_t* cache_index,
                           float sm_scale, void* stream);
 
+/* ---- block-table (paged) caches -----------------------------------------
+ * "10.3 - KV cache implementation details", section 7.2: the cache is
+ * allocated in fixed-size blocks, like virtual-memory pages, and a block
+ * table maps each sequence's logical blocks to physical ones, so
+ * non-contiguous blocks are logically contiguous; section 7.3: sequences
+ * that share a prefix can share its blocks.
+ *
+ * A paged cache is a bf16 GQA cache whose desc.max_context is the logical
+ * row capacity of one sequence (a multiple of block_size, at most 4096
+ * blocks). block_size is a power of two in [16, 256]; num_blocks >= 1
+ * physical blocks per layer, and one layer's K pool (num_blocks * n_kv_heads
+ * * block_size * head_dim * 2 bytes) must stay below 2^30 bytes
+ * (KVC_ERR_UNSUPPORTED otherwise). Layout:
+ *   [n_layers][2 (K, V)][num_blocks][n_kv_heads][block_size][head_dim].
+ * A block table is a device int32 array [batch][max_context / block_size]:
+ * row r of sequence b is row r % block_size of physical block
+ * table[b][r / block_size]. Tables are passed per call, so they can change
+ * between steps; entries for rows a call does not touch are never read.
+ * Sharing a block between sequences shares its rows (an append into it is
+ * seen by all of them; two sequences that write the same row in one call
+ * race, and the row holds one of the two writes). On a paged cache only the
+ * calls below, kvc_layer_ptrs (the two pools), kvc_logical_bytes,
+ * kvc_set/get_workgroups, kvc_check and kvc_free apply; the others return
+ * KVC_ERR_INVALID_ARG. */
+
+/* Physical bytes of a paged cache: 2 * n_layers * num_blocks * n_kv_heads
+ * * block_size * head_dim * 2. Pure host. */
+kvc_status kvc_bytes_paged(const kvc_desc* desc, int32_t block_size, int32_t num_blocks, uint64_t* physical);
+
+/* Allocate a paged cache (pools zero-filled unless external), as kvc_alloc. */
+kvc_status kvc_alloc_paged(const kvc_desc* desc, int32_t block_size, int32_t num_blocks, void* external,
+                           kvc_cache** out);
+
+/* kvc_append through a block table: rows [cache_index[b], cache_index[b] +
+ * t_new) of sequence b get k_new[b], v_new[b] ([B][H_kv][t_new][d_h]). A
+ * sequence whose rows leave [0, max_context), or reach a table entry outside
+ * [0, num_blocks), is skipped (nothing written) and raises the device-range
+ * flag. With t_new > 1 this is also the prefill fill of a paged cache. */
+kvc_status kvc_paged_append(kvc_cache* cache, int32_t layer, const void* k_new, const void* v_new,
+                            const int32_t* block_table, const int32_t* cache_index, int32_t t_new, void* stream);
+
+/* kvc_decode_attn through a block table: the same attention over the rows
+ * [0, n_b) the table maps. A row whose entry lies outside [0, num_blocks)
+ * reads as zeros and raises the device-range flag. */
+kvc_status kvc_paged_decode_attn(kvc_cache* cache, int32_t layer, const void* q, void* out,
+                                 const int32_t* block_table, const int32_t* valid_lens,
+                                 const int32_t* cache_index, float sm_scale, void* stream);
+
 /* Force the number of persistent workgroups attention launches (0 restores
  * the default: one per compute unit). The rows of
  * all sequences and kv heads are divided evenly among them, so this only

@@ -121,6 +121,40 @@ kvc_status after_launch(kvc_cache* c, hipError_t e, hipStream_t stream) {
 
 bool layer_ok(const kvc_cache* c, int32_t layer) { return layer >= 0 && layer < c->d.n_layers; }
 
+// Static-cache calls: a live, non-paged cache and a layer in range.
+bool static_ok(const kvc_cache* c, int32_t layer) { return c && !c->paged && layer_ok(c, layer); }
+
+int log2_exact(int x) {
+  int s = 0;
+  while ((1 << s) < x) ++s;
+  return (1 << s) == x ? s : -1;
+}
+
+// Block-table caches ("10.3 - KV cache implementation details", section
+// 7.2): bf16 GQA pools of num_blocks blocks of block_size rows per kv head.
+kvc_status validate_paged(const kvc_desc* d, int32_t block_size, int32_t num_blocks) {
+  kvc_status s = validate_desc(d);
+  if (s != KVC_OK) return s;
+  if (block_size < 1 || num_blocks < 1) return KVC_ERR_INVALID_ARG;
+  if (d->max_context % block_size != 0) return KVC_ERR_INVALID_ARG;
+  if (d->attn != KVC_ATTN_GQA || d->dtype != KVC_BF16) return KVC_ERR_UNSUPPORTED;
+  // a 16-row attention tile spans at most two blocks
+  if (block_size < 16 || block_size > 256 || log2_exact(block_size) < 0) return KVC_ERR_UNSUPPORTED;
+  if (d->max_context / block_size > KVC_MAX_TABLE) return KVC_ERR_UNSUPPORTED;
+  // byte offsets within one pool are 32-bit, with room above for "no row"
+  if ((int64_t)num_blocks * d->n_kv_heads * block_size * d->head_dim * 2 >= (int64_t)1 << 30)
+    return KVC_ERR_UNSUPPORTED;
+  return KVC_OK;
+}
+
+uint64_t paged_bytes(const kvc_desc* d, int32_t block_size, int32_t num_blocks) {
+  // 2 * L * num_blocks * H_kv * block_size * d_h * 2 (each pool < 2^30 bytes)
+  return 2ull * d->n_layers * ((uint64_t)num_blocks * d->n_kv_heads * block_size * d->head_dim * 2);
+}
+
+kvc_status alloc_impl(const kvc_desc* desc, void* external, uint64_t bytes, int32_t block_size,
+                      int32_t num_blocks, kvc_cache** out);
+
 }  // namespace
 
 extern "C" {
@@ -137,11 +171,38 @@ kvc_status kvc_alloc(const kvc_desc* desc, void* external, kvc_cache** out) {
   *out = nullptr;
   kvc_status s = validate_desc(desc);
   if (s != KVC_OK) return s;
-  if (external && ((uintptr_t)external % 256) != 0) return KVC_ERR_INVALID_ARG;
   uint64_t bytes = 0;
   s = bytes_of(desc, &bytes);
   if (s != KVC_OK) return s;
+  return alloc_impl(desc, external, bytes, 0, 0, out);
+}
 
+kvc_status kvc_bytes_paged(const kvc_desc* desc, int32_t block_size, int32_t num_blocks, uint64_t* physical) {
+  if (!physical) return KVC_ERR_INVALID_ARG;
+  kvc_status s = validate_paged(desc, block_size, num_blocks);
+  if (s != KVC_OK) return s;
+  *physical = paged_bytes(desc, block_size, num_blocks);
+  return KVC_OK;
+}
+
+kvc_status kvc_alloc_paged(const kvc_desc* desc, int32_t block_size, int32_t num_blocks, void* external,
+                           kvc_cache** out) {
+  if (!out) return KVC_ERR_INVALID_ARG;
+  *out = nullptr;
+  kvc_status s = validate_paged(desc, block_size, num_blocks);
+  if (s != KVC_OK) return s;
+  return alloc_impl(desc, external, paged_bytes(desc, block_size, num_blocks), block_size, num_blocks, out);
+}
+
+}  // extern "C"
+
+namespace {
+
+// One allocation of `bytes` (or the caller's buffer) plus the decode
+// workspace; block_size = 0 for a static cache.
+kvc_status alloc_impl(const kvc_desc* desc, void* external, uint64_t bytes, int32_t block_size,
+                      int32_t num_blocks, kvc_cache** out) {
+  if (external && ((uintptr_t)external % 256) != 0) return KVC_ERR_INVALID_ARG;
   kvc_cache* c = new (std::nothrow) kvc_cache();
   if (!c) return KVC_ERR_OOM;
   memset(c, 0, sizeof(*c));
@@ -154,7 +215,16 @@ kvc_status kvc_alloc(const kvc_desc* desc, void* external, kvc_cache** out) {
   if (hipGetDeviceProperties(&prop, c->device) != hipSuccess) { delete c; return KVC_ERR_DEVICE; }
   c->num_cus = prop.multiProcessorCount;
 
-  if (desc->attn == KVC_ATTN_GQA) {
+  if (block_size > 0) {
+    c->paged = true;
+    c->block_size = block_size;
+    c->block_shift = log2_exact(block_size);
+    c->num_blocks = num_blocks;
+    c->table_width = desc->max_context / block_size;
+    c->row_elems = desc->head_dim;
+    c->kv_bytes = (uint64_t)num_blocks * desc->n_kv_heads * block_size * desc->head_dim * c->elem;
+    c->layer_bytes = 2 * c->kv_bytes;
+  } else if (desc->attn == KVC_ATTN_GQA) {
     c->row_elems = desc->head_dim;
     c->kv_bytes = (uint64_t)desc->batch * desc->n_kv_heads * desc->max_context * desc->head_dim * c->elem;
     c->layer_bytes = 2 * c->kv_bytes;
@@ -204,6 +274,10 @@ kvc_status kvc_alloc(const kvc_desc* desc, void* external, kvc_cache** out) {
   return KVC_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
 kvc_status kvc_free(kvc_cache* c) {
   if (!c) return KVC_OK;
   hipError_t e = hipDeviceSynchronize();
@@ -227,7 +301,7 @@ kvc_status kvc_layer_ptrs(const kvc_cache* c, int32_t layer, void** k, void** v)
 }
 
 kvc_status kvc_layer_scales(const kvc_cache* c, int32_t layer, void** k_scales, void** v_scales) {
-  if (!c || !k_scales || !v_scales || !layer_ok(c, layer) || c->d.dtype != KVC_I8) return KVC_ERR_INVALID_ARG;
+  if (!k_scales || !v_scales || !static_ok(c, layer) || c->d.dtype != KVC_I8) return KVC_ERR_INVALID_ARG;
   uint8_t* l = c->scales + (uint64_t)layer * c->scale_layer_bytes;
   *k_scales = l;
   *v_scales = l + c->scale_kv_bytes;
@@ -250,7 +324,7 @@ kvc_status kvc_logical_bytes(const kvc_cache* c, const int32_t* host_valid_lens,
 
 kvc_status kvc_prefill_fill(kvc_cache* c, int32_t layer, const void* k, const void* v, int32_t start,
                             int32_t t, void* stream) {
-  if (!c || !k || !layer_ok(c, layer)) return KVC_ERR_INVALID_ARG;
+  if (!k || !static_ok(c, layer)) return KVC_ERR_INVALID_ARG;
   const bool gqa = c->d.attn == KVC_ATTN_GQA;
   if (gqa ? !v : v != nullptr) return KVC_ERR_INVALID_ARG;
   if (t < 1) return KVC_ERR_INVALID_ARG;
@@ -275,7 +349,7 @@ kvc_status kvc_prefill_fill(kvc_cache* c, int32_t layer, const void* k, const vo
 
 kvc_status kvc_append(kvc_cache* c, int32_t layer, const void* k_new, const void* v_new,
                       const int32_t* cache_index, int32_t t_new, void* stream) {
-  if (!c || !k_new || !cache_index || !layer_ok(c, layer)) return KVC_ERR_INVALID_ARG;
+  if (!k_new || !cache_index || !static_ok(c, layer)) return KVC_ERR_INVALID_ARG;
   const bool gqa = c->d.attn == KVC_ATTN_GQA;
   if (gqa ? !v_new : v_new != nullptr) return KVC_ERR_INVALID_ARG;
   if (t_new < 1) return KVC_ERR_INVALID_ARG;
@@ -301,7 +375,7 @@ kvc_status kvc_append(kvc_cache* c, int32_t layer, const void* k_new, const void
 kvc_status kvc_decode_attn(kvc_cache* c, int32_t layer, const void* q, void* out,
                            const int32_t* valid_lens, const int32_t* cache_index, float sm_scale,
                            void* stream) {
-  if (!c || !q || !out || !layer_ok(c, layer)) return KVC_ERR_INVALID_ARG;
+  if (!q || !out || !static_ok(c, layer)) return KVC_ERR_INVALID_ARG;
   if (!valid_lens && !cache_index) return KVC_ERR_INVALID_ARG;
   if (!(sm_scale > 0.0f) || sm_scale > 3.0e38f) return KVC_ERR_INVALID_ARG;
   void* kl;
@@ -323,7 +397,7 @@ kvc_status kvc_decode_attn(kvc_cache* c, int32_t layer, const void* q, void* out
 
 kvc_status kvc_prefill_attn(kvc_cache* c, int32_t layer, const void* q, const void* k, const void* v, void* out,
                             int32_t start, int32_t t, float sm_scale, void* stream) {
-  if (!c || !q || !k || !v || !out || !layer_ok(c, layer)) return KVC_ERR_INVALID_ARG;
+  if (!q || !k || !v || !out || !static_ok(c, layer)) return KVC_ERR_INVALID_ARG;
   if (c->d.attn != KVC_ATTN_GQA || c->d.dtype != KVC_BF16) return KVC_ERR_UNSUPPORTED;
   if (t < 1) return KVC_ERR_INVALID_ARG;
   if (start < 0 || (int64_t)start + t > c->d.max_context) return KVC_ERR_CAPACITY;
@@ -341,7 +415,7 @@ kvc_status kvc_prefill_attn(kvc_cache* c, int32_t layer, const void* q, const vo
 kvc_status kvc_append_decode_attn(kvc_cache* c, int32_t layer, const void* k_new, const void* v_new,
                                   const void* q, void* out, const int32_t* cache_index, float sm_scale,
                                   void* stream) {
-  if (!c || !k_new || !v_new || !q || !out || !cache_index || !layer_ok(c, layer)) return KVC_ERR_INVALID_ARG;
+  if (!k_new || !v_new || !q || !out || !cache_index || !static_ok(c, layer)) return KVC_ERR_INVALID_ARG;
   if (c->d.attn != KVC_ATTN_GQA) return KVC_ERR_UNSUPPORTED;
   if (!(sm_scale > 0.0f) || sm_scale > 3.0e38f) return KVC_ERR_INVALID_ARG;
   void* kl;
@@ -358,7 +432,7 @@ kvc_status kvc_append_decode_attn(kvc_cache* c, int32_t layer, const void* k_new
 kvc_status kvc_mla_decode(kvc_cache* c, int32_t layer, const void* q_nope, const void* q_rope,
                           const void* w_uk, const void* w_uv, void* out, const int32_t* valid_lens,
                           const int32_t* cache_index, float sm_scale, void* stream) {
-  if (!c || !q_nope || !q_rope || !w_uk || !w_uv || !out || !layer_ok(c, layer))
+  if (!q_nope || !q_rope || !w_uk || !w_uv || !out || !static_ok(c, layer))
     return KVC_ERR_INVALID_ARG;
   if (c->d.attn != KVC_ATTN_MLA) return KVC_ERR_INVALID_ARG;
   if (!valid_lens && !cache_index) return KVC_ERR_INVALID_ARG;
@@ -371,6 +445,37 @@ kvc_status kvc_mla_decode(kvc_cache* c, int32_t layer, const void* q_nope, const
   if (e == hipSuccess)
     e = kvc_launch_mla_attn(c, kl, c->ws_qabs, c->ws_olat, valid_lens, cache_index, sm_scale, s);
   if (e == hipSuccess) e = kvc_launch_mla_uproj(c, c->ws_olat, w_uv, out, s);
+  return after_launch(c, e, s);
+}
+
+kvc_status kvc_paged_append(kvc_cache* c, int32_t layer, const void* k_new, const void* v_new,
+                            const int32_t* block_table, const int32_t* cache_index, int32_t t_new, void* stream) {
+  if (!c || !c->paged || !layer_ok(c, layer) || !k_new || !v_new || !block_table || !cache_index)
+    return KVC_ERR_INVALID_ARG;
+  if (t_new < 1) return KVC_ERR_INVALID_ARG;
+  if (t_new > c->d.max_context) return KVC_ERR_CAPACITY;
+  uint8_t* kl;
+  uint8_t* vl;
+  kvc_layer_ptrs(c, layer, (void**)&kl, (void**)&vl);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = kvc_launch_paged_rows(k_new, v_new, kl, vl, block_table, c->d.batch, c->d.n_kv_heads, t_new,
+                                       c->row_elems * c->elem, c->block_shift, c->num_blocks, c->table_width,
+                                       c->d.max_context, cache_index, c->err_flag, s);
+  return after_launch(c, e, s);
+}
+
+kvc_status kvc_paged_decode_attn(kvc_cache* c, int32_t layer, const void* q, void* out,
+                                 const int32_t* block_table, const int32_t* valid_lens,
+                                 const int32_t* cache_index, float sm_scale, void* stream) {
+  if (!c || !c->paged || !layer_ok(c, layer) || !q || !out || !block_table) return KVC_ERR_INVALID_ARG;
+  if (!valid_lens && !cache_index) return KVC_ERR_INVALID_ARG;
+  if (!(sm_scale > 0.0f) || sm_scale > 3.0e38f) return KVC_ERR_INVALID_ARG;
+  void* kl;
+  void* vl;
+  kvc_layer_ptrs(c, layer, &kl, &vl);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = kvc_launch_gqa_decode(c, kl, vl, q, out, valid_lens, cache_index, sm_scale, s, nullptr, nullptr,
+                                       nullptr, nullptr, block_table);
   return after_launch(c, e, s);
 }
 

@@ -1,6 +1,7 @@
-// Row copies into the static cache: the prefill fill (rows [start, start+t)
-// of every sequence) and the in-place decode append (rows
-// [cache_index[b], cache_index[b] + t_new) of sequence b).
+// Row copies into the cache: the prefill fill (rows [start, start+t) of
+// every sequence) and the in-place decode append (rows
+// [cache_index[b], cache_index[b] + t_new) of sequence b), into the static
+// buffer or through a block table.
 //
 // "KV Cache Optimization: GQA Audit, In-Place Buffers, Persistent Prompts",
 // "#2 In-place KV cache updates", "After": the new rows are slice-assigned
@@ -40,7 +41,65 @@ __global__ __launch_bounds__(256) void copy_rows_kernel(
   if (src_v) dst_v[dst] = src_v[i];
 }
 
+// Append through a block table ("10.3 - KV cache implementation details",
+// section 7.2): row r of sequence b goes to row r % block_size of physical
+// block table[b][r / block_size], pool layout [num_blocks][G][block_size][row].
+// Grid (ceil(G t row_vecs / 256), B): every workgroup of sequence b first
+// checks that the rows fit and that every table entry they reach lies in
+// the pool (a few entries per thread), so the whole sequence is written or
+// skipped; then each thread copies one 16-byte vector of K and of V.
+__global__ __launch_bounds__(256) void paged_rows_kernel(
+    const uint4* __restrict__ src_k, const uint4* __restrict__ src_v, uint4* __restrict__ pool_k,
+    uint4* __restrict__ pool_v, const int32_t* __restrict__ table, int groups, int t, int row_vecs,
+    int block_shift, int num_blocks, int table_width, int max_context, const int32_t* __restrict__ dev_start,
+    int32_t* __restrict__ err_flag) {
+  const int b = blockIdx.y;
+  const int start = dev_start[b];
+  const int32_t* trow = table + (long)b * table_width;
+  bool bad = start < 0 || (long)start + t > max_context;  // the same in every thread
+  if (!bad) {
+    const int first = start >> block_shift;
+    const int last = (start + t - 1) >> block_shift;
+    int any = 0;
+    for (int i = first + (int)threadIdx.x; i <= last; i += 256) any |= trow[i] < 0 || trow[i] >= num_blocks;
+    bad = __syncthreads_or(any) != 0;
+  }
+  if (bad) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(err_flag, 1);
+    return;
+  }
+  const long per_seq = (long)groups * t * row_vecs;
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= per_seq) return;
+  const long per_group = (long)t * row_vecs;
+  const int g = (int)(i / per_group);
+  const int rem = (int)(i - g * per_group);
+  const int row = rem / row_vecs;
+  const int vec = rem - row * row_vecs;
+  const int r = start + row;
+  const long blk = trow[r >> block_shift];
+  const long dst = (((blk * groups + g) << block_shift) + (r & ((1 << block_shift) - 1))) * row_vecs + vec;
+  const long src = (long)b * per_seq + i;
+  pool_k[dst] = src_k[src];
+  pool_v[dst] = src_v[src];
+}
+
 }  // namespace
+
+hipError_t kvc_launch_paged_rows(const void* src_k, const void* src_v, uint8_t* pool_k, uint8_t* pool_v,
+                                 const int32_t* table, int batch, int n_kv_heads, int t, int row_bytes,
+                                 int block_shift, int num_blocks, int table_width, int max_context,
+                                 const int32_t* dev_start, int32_t* err_flag, hipStream_t stream) {
+  if (row_bytes % 16 != 0 || !dev_start || !table) return hipErrorInvalidValue;
+  const int row_vecs = row_bytes / 16;
+  const long per_seq = (long)n_kv_heads * t * row_vecs;
+  const long blocks = (per_seq + 255) / 256;
+  if (blocks > 0x7fffffffL || batch > 65535) return hipErrorInvalidValue;
+  paged_rows_kernel<<<dim3((unsigned)blocks, (unsigned)batch), dim3(256), 0, stream>>>(
+      (const uint4*)src_k, (const uint4*)src_v, (uint4*)pool_k, (uint4*)pool_v, table, n_kv_heads, t, row_vecs,
+      block_shift, num_blocks, table_width, max_context, dev_start, err_flag);
+  return hipGetLastError();
+}
 
 hipError_t kvc_launch_copy_rows(const void* src_k, const void* src_v, uint8_t* dst_k, uint8_t* dst_v,
                                 int batch, int n_kv_heads, int t, int row_bytes, int max_context,

@@ -151,6 +151,11 @@ struct DecodeArgs {
   // from the cache, and written into the cache by the piece that ends there.
   const void* k_new;
   const void* v_new;
+  // Block-table caches (null otherwise): k and v are the layer's pools
+  // [num_blocks][H_kv][block_size][D] of pool_bytes bytes each, and row r of
+  // sequence b lives in block table[b * table_width + (r >> block_shift)].
+  const int32_t* table;
+  int block_shift, num_blocks, table_width, pool_bytes;
 };
 
 // Fused append: the piece of segment (b, g, chunk) that ends at the
@@ -509,11 +514,24 @@ struct ValuPiece {
 
 
 
+// Byte offset that lies past every pool (pools are < 2^30 bytes): buffer
+// loads from it and from anything up to 2^30 beyond return zeros.
+constexpr int kNoRow = 1 << 30;
+
 // bf16 piece on the matrix cores (see the file comment). Lane l of a wave is
 // (g, j) = (l / 16, l % 16). MFMA 16x16x32: A lane holds A[j][8g..8g+7],
 // B lane holds B[8g..8g+7][j], D lane holds D[4g..4g+3][j]; 16x16x16: the
 // same with 4g..4g+3 in place of 8g..8g+7.
-template <int D>
+//
+// PAGED: the same piece over a block-table cache ("10.3 - KV cache
+// implementation details", section 7.2). At the start of a piece the
+// workgroup copies the table entries of the piece's rows into LDS as byte
+// offsets of the blocks' (kv head) row groups in the pool (kNoRow for an
+// entry outside the pool, which also raises the device flag). A 16-row tile
+// spans at most two blocks (block_size >= 16), so each tile reads two
+// offsets and every lane forms the offsets of the rows it loads; rows past
+// the piece get kNoRow, which reads as zeros as the static piece's tail does.
+template <int D, bool PAGED = false>
 struct MfmaPiece {
   using Elem = uint16_t;
   static constexpr int kD = D;
@@ -530,10 +548,14 @@ struct MfmaPiece {
   static constexpr int NBUF = D <= 64 ? 3 : 2; // register tiles in the ring (register budget)
 #endif
   static_assert(D % 32 == 0 && VCH >= 1 && TR * CPR % 64 == 0, "head_dim must be 32..256");
+  static constexpr int kTable = PAGED ? KVC_MAX_TABLE : 1;
 
   struct Smem {
     union {
-      unsigned char v[kWaves][TR * VSTRIDE];  // per-wave V staging (tile loop)
+      struct {
+        unsigned char v[kWaves][TR * VSTRIDE];  // per-wave V staging (tile loop)
+        int32_t blk[kTable];                    // block-table caches: block offsets of the piece's rows
+      } t;
       struct {
         float acc[kWaves][16][D];
         float m[kWaves][16];
@@ -571,7 +593,7 @@ struct MfmaPiece {
     const size_t row0 = ((size_t)b * a.n_kv_heads + kvg) * (size_t)a.max_context;
     const uint16_t* kbase = reinterpret_cast<const uint16_t*>(a.k) + row0 * D;
     const uint16_t* vbase = reinterpret_cast<const uint16_t*>(a.v) + row0 * D;
-    unsigned char* vs = sm.u.v[wave];
+    unsigned char* vs = sm.u.t.v[wave];
 
     // Buffer resources spanning exactly the valid rows [0, r_end) of this
     // (sequence, kv head): loads of rows past the end (the tail of the last
@@ -579,16 +601,55 @@ struct MfmaPiece {
     // and their scores are masked below.
     // Fused append: the new row `fresh` lies outside the resources (it reads
     // as zeros) and is taken from k_new / v_new by the lanes that hold it.
-    const int fresh = uniform(fused_row(a, r_end, n));
+    const int fresh = PAGED ? -1 : uniform(fused_row(a, r_end, n));
     const int r_cache = fresh >= 0 ? fresh : r_end;  // rows read from the cache
-    const __amdgpu_buffer_rsrc_t kres = buffer_rsrc(kbase, r_cache * (2 * D));
-    const __amdgpu_buffer_rsrc_t vres = buffer_rsrc(vbase, r_cache * (2 * D));
+    const __amdgpu_buffer_rsrc_t kres = PAGED ? buffer_rsrc(a.k, a.pool_bytes) : buffer_rsrc(kbase, r_cache * (2 * D));
+    const __amdgpu_buffer_rsrc_t vres = PAGED ? buffer_rsrc(a.v, a.pool_bytes) : buffer_rsrc(vbase, r_cache * (2 * D));
     const int koff = j * (2 * D) + 16 * g;  // K row base + j, dims 8g.. of each 32-dim step
     const int voff = lane * 16;             // V tile as contiguous 16-byte chunks
     const uint16_t* knew = reinterpret_cast<const uint16_t*>(a.k_new) + ((size_t)b * a.n_kv_heads + kvg) * D;
     const uint16_t* vnew = reinterpret_cast<const uint16_t*>(a.v_new) + ((size_t)b * a.n_kv_heads + kvg) * D;
 
+    // Block-table caches: the piece's table slice, as block offsets in LDS.
+    const int shift = PAGED ? uniform(a.block_shift) : 0;
+    const int blk0 = r_begin >> shift;
+    const int nblk = ((r_end - 1) >> shift) - blk0 + 1;
+    if constexpr (PAGED) {
+      const int32_t* trow = a.table + (size_t)b * a.table_width + blk0;
+      const int grp_bytes = (2 * D) << shift;  // one kv head's rows of one block
+      for (int i = threadIdx.x; i < nblk; i += kThreads) {
+        const int e = trow[i];
+        const bool ok = e >= 0 && e < a.num_blocks;
+        if (!ok) atomicOr(a.err_flag, 1);
+        sm.u.t.blk[i] = ok ? (e * a.n_kv_heads + kvg) * grp_bytes : kNoRow;
+      }
+      __syncthreads();
+    }
+    // Byte offset of row r of the tile at `base` (r < base + TR), given the
+    // offsets of the tile's first and second block.
+    auto paged_row = [&](int base, int r, int off0, int off1) {
+      const int off = ((r >> shift) == (base >> shift)) ? off0 : off1;
+      return r < r_end ? off + ((r & ((1 << shift) - 1)) * (2 * D)) : kNoRow;
+    };
+
     auto load_tile = [&](int base, bf16x8_t (&kr)[KS], u32x4_t (&vr)[VCH]) {
+      if constexpr (PAGED) {
+        // base >= r_begin; a tile past the piece reads clamped entries and
+        // all its rows get kNoRow
+        const int off0 = sm.u.t.blk[min((base >> shift) - blk0, nblk - 1)];
+        const int off1 = sm.u.t.blk[min(((base + TR - 1) >> shift) - blk0, nblk - 1)];
+        const int kb = paged_row(base, base + j, off0, off1) + 16 * g;
+#pragma unroll
+        for (int k = 0; k < KS; ++k)
+          kr[k] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(kres, kb + 64 * k, 0, 0));
+#pragma unroll
+        for (int i = 0; i < VCH; ++i) {
+          const int f = i * 64 + lane;
+          const int vb = paged_row(base, base + f / CPR, off0, off1) + (f % CPR) * 16;
+          vr[i] = __builtin_amdgcn_raw_buffer_load_b128(vres, vb, 0, 0);
+        }
+        return;
+      }
       const int kb = base * (2 * D) + koff;
 #pragma unroll
       for (int k = 0; k < KS; ++k)
@@ -691,7 +752,7 @@ struct MfmaPiece {
       }
     }
 
-    fused_write<uint16_t, D>(a, b, kvg, chunk, fresh);
+    if constexpr (!PAGED) fused_write<uint16_t, D>(a, b, kvg, chunk, fresh);
     combine(a, sm, o, m, l, b, h0, whole, slot);
   }
 
@@ -849,7 +910,7 @@ struct I8Piece {
     }
     const int koff = j * D + g * (D / 4);  // row j, this lane's quarter of the dims
     const int voff = lane * 16;            // V tile as contiguous 16-byte vectors
-    unsigned char* vs = sm.u.v[wave];
+    unsigned char* vs = sm.u.t.v[wave];
 
     auto load_tile = [&](int base, Tile& tl) {
       const int kb = base * D + koff;
@@ -1106,6 +1167,15 @@ hipError_t launch_bf16(const kvc_cache* c, const DecodeArgs& a, hipStream_t st) 
   return launch_piece<MfmaPiece<D>, uint16_t, D>(c, a, gc, st);
 }
 
+// bf16 block-table cache: the paged matrix-core piece, chunks as for bf16.
+template <int D>
+hipError_t launch_paged(const kvc_cache* c, const DecodeArgs& a, hipStream_t st) {
+  const int group = c->d.n_heads / c->d.n_kv_heads;
+  int gc = group <= 16 ? group : 16;
+  while (group % gc != 0) --gc;
+  return launch_piece<MfmaPiece<D, true>, uint16_t, D>(c, a, gc, st);
+}
+
 // int8: matrix-core piece over codes; chunks of at most 16 heads as bf16.
 template <int D>
 hipError_t launch_i8(const kvc_cache* c, const DecodeArgs& a, hipStream_t st) {
@@ -1131,7 +1201,7 @@ hipError_t kvc_launch_gqa_decode(const kvc_cache* c, const void* k_layer, const 
                                  const void* q, void* out, const int32_t* valid_lens,
                                  const int32_t* cache_index, float sm_scale, hipStream_t stream,
                                  const void* k_new, const void* v_new, const float* k_scale,
-                                 const float* v_scale) {
+                                 const float* v_scale, const int32_t* block_table) {
   if (c->d.batch > KVC_MAX_BATCH || (long long)c->d.batch * c->d.n_heads > 0x7fffffffLL)
     return hipErrorInvalidValue;
   DecodeArgs a;
@@ -1157,6 +1227,23 @@ hipError_t kvc_launch_gqa_decode(const kvc_cache* c, const void* k_layer, const 
   a.v_new = v_new;
   a.k_scale = k_scale;
   a.v_scale = v_scale;
+  a.table = block_table;
+  a.block_shift = c->block_shift;
+  a.num_blocks = c->num_blocks;
+  a.table_width = c->table_width;
+  a.pool_bytes = (int)c->kv_bytes;
+  if (c->paged) {
+    if (!block_table || c->d.dtype != KVC_BF16 || k_new || c->table_width > KVC_MAX_TABLE ||
+        c->kv_bytes >= (1ull << 30))
+      return hipErrorInvalidValue;
+    switch (c->d.head_dim) {
+      case 32: return launch_paged<32>(c, a, stream);
+      case 64: return launch_paged<64>(c, a, stream);
+      case 128: return launch_paged<128>(c, a, stream);
+      case 256: return launch_paged<256>(c, a, stream);
+    }
+    return hipErrorInvalidValue;
+  }
   if (c->d.dtype == KVC_I8) {
     if (!k_scale || !v_scale) return hipErrorInvalidValue;
     switch (c->d.head_dim) {

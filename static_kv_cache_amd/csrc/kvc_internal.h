@@ -27,6 +27,8 @@ struct kvc_cache {
   uint64_t scale_layer_bytes;  // int8: bytes of one layer's K and V scales (0 otherwise)
   uint64_t scale_kv_bytes;     // int8: offset of the V scales from the K scales in a layer
   uint8_t* scales;        // int8: [L][2][B][H_kv][S] float32 scales (after the codes), else NULL
+  bool paged;             // block-table cache: layer = [K|V][num_blocks][H_kv][block_size][d_h]
+  int block_size, block_shift, num_blocks, table_width;  // table_width = max_context / block_size
 
   // fixed workspace (allocated once by kvc_alloc)
   int max_workgroups;     // num_cus * KVC_MAX_WG_PER_CU
@@ -52,6 +54,18 @@ hipError_t kvc_launch_copy_rows(const void* src_k, const void* src_v, uint8_t* d
                                 const int32_t* dev_start, int host_start, int32_t* err_flag,
                                 hipStream_t stream);
 
+// Largest block table slice one decode piece keeps in LDS (blocks per sequence).
+#define KVC_MAX_TABLE 4096
+
+// Row copy into a paged cache: rows [start_b, start_b + t) of sequence b
+// through table[b] (table_width entries per sequence); a sequence whose rows
+// leave [0, max_context) or reach an entry outside [0, num_blocks) is skipped
+// and raises *err_flag.
+hipError_t kvc_launch_paged_rows(const void* src_k, const void* src_v, uint8_t* pool_k, uint8_t* pool_v,
+                                 const int32_t* table, int batch, int n_kv_heads, int t, int row_bytes,
+                                 int block_shift, int num_blocks, int table_width, int max_context,
+                                 const int32_t* dev_start, int32_t* err_flag, hipStream_t stream);
+
 // Quantising row copy into an int8 cache: as kvc_launch_copy_rows for bf16
 // source rows [B][H_kv][t][d] (d = head_dim), writing each row's int8 codes
 // to dst_k / dst_v ([B][H_kv][S][d]) and its float32 scale to ks / vs
@@ -69,7 +83,8 @@ hipError_t kvc_launch_gqa_decode(const kvc_cache* c, const void* k_layer, const 
                                  const void* q, void* out, const int32_t* valid_lens,
                                  const int32_t* cache_index, float sm_scale, hipStream_t stream,
                                  const void* k_new = nullptr, const void* v_new = nullptr,
-                                 const float* k_scale = nullptr, const float* v_scale = nullptr);
+                                 const float* k_scale = nullptr, const float* v_scale = nullptr,
+                                 const int32_t* block_table = nullptr);
 
 // Causal prefill attention of a chunk [start, start + t) whose rows are
 // already in the cache (bf16 GQA): q, out = [B][H][t][D].

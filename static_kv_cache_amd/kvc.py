@@ -57,6 +57,10 @@ _SIGS = {
     "kvc_mla_decode": [_p, _i32, _p, _p, _p, _p, _p, _p, _p, ctypes.c_float, _p],
     "kvc_append_decode_attn": [_p, _i32, _p, _p, _p, _p, _p, ctypes.c_float, _p],
     "kvc_prefill_attn": [_p, _i32, _p, _p, _p, _p, _i32, _i32, ctypes.c_float, _p],
+    "kvc_bytes_paged": [ctypes.POINTER(Desc), _i32, _i32, ctypes.POINTER(ctypes.c_uint64)],
+    "kvc_alloc_paged": [ctypes.POINTER(Desc), _i32, _i32, _p, ctypes.POINTER(_p)],
+    "kvc_paged_append": [_p, _i32, _p, _p, _p, _p, _i32, _p],
+    "kvc_paged_decode_attn": [_p, _i32, _p, _p, _p, _p, _p, ctypes.c_float, _p],
     "kvc_set_workgroups": [_p, _i32],
     "kvc_get_workgroups": [_p, ctypes.POINTER(_i32), ctypes.POINTER(_i32)],
     "kvc_check": [_p, _p],
@@ -352,6 +356,76 @@ class Cache:
             self.free()
         except Exception:
             pass
+
+
+def paged_cache_bytes(desc, block_size, num_blocks):
+    out = ctypes.c_uint64(0)
+    _call("kvc_bytes_paged", ctypes.byref(desc), block_size, num_blocks, ctypes.byref(out))
+    return out.value
+
+
+class PagedCache(Cache):
+    """A block-table cache (kvc_alloc_paged): per layer, K and V pools
+    [num_blocks, H_kv, block_size, D] (bf16); block tables [B, max_context // block_size]
+    int32 are passed per call. Only the paged calls (and the shared ones: layer
+    pointers, workgroups, check, free) apply."""
+
+    def __init__(self, desc, block_size, num_blocks, external=None):
+        torch = _torch()
+        self.desc = desc
+        self.dtype = {KVC_F32: "f32", KVC_BF16: "bf16", KVC_I8: "i8"}[desc.dtype]
+        self.io_dtype = io_dtype(self.dtype)
+        self.device = torch.device("cuda", torch.cuda.current_device())
+        self.block_size = block_size
+        self.num_blocks = num_blocks
+        self.table_width = desc.max_context // block_size
+        self.nbytes = paged_cache_bytes(desc, block_size, num_blocks)
+        self._external = external
+        ext = None
+        if external is not None:
+            if not (external.is_cuda and external.is_contiguous()
+                    and external.numel() * external.element_size() >= self.nbytes):
+                raise ValueError("external buffer must be a contiguous device tensor of >= kvc_bytes_paged")
+            ext = ctypes.c_void_p(external.data_ptr())
+        h = ctypes.c_void_p()
+        _call("kvc_alloc_paged", ctypes.byref(desc), block_size, num_blocks, ext, ctypes.byref(h))
+        self._h = h
+
+    def layer_tensors(self, layer):
+        """Copies of one layer's pools (K, V) as [num_blocks, H_kv, block_size, D] tensors."""
+        torch = _torch()
+        d = self.desc
+        shape = (self.num_blocks, d.n_kv_heads, self.block_size, d.head_dim)
+        out = []
+        for ptr in self.layer_ptrs(layer):
+            t = torch.empty(shape, dtype=torch_dtype(self.dtype), device=self.device)
+            _memcpy_d2d(t.data_ptr(), ptr, t.numel() * t.element_size(), self.device)
+            out.append(t)
+        return tuple(out)
+
+    def _table(self, table):
+        return self._check(table, (self.desc.batch, self.table_width), _torch().int32, "block_table")
+
+    def paged_append(self, layer, k_new, v_new, block_table, cache_index):
+        """Write rows [cache_index[b], cache_index[b] + t) of each sequence through its table
+        (kvc_paged_append): k_new, v_new [B, H_kv, t, D]."""
+        d = self.desc
+        t = k_new.shape[2]
+        shape = (d.batch, d.n_kv_heads, t, d.head_dim)
+        kp, vp = self._check(k_new, shape, name="k_new"), self._check(v_new, shape, name="v_new")
+        _call("kvc_paged_append", self.handle, layer, kp, vp, self._table(block_table),
+              self._idx(cache_index, "cache_index"), t, _stream(self.device))
+
+    def paged_decode_attn(self, layer, q, out, block_table, valid_lens=None, cache_index=None, sm_scale=None):
+        """Decode attention over the rows the tables map (kvc_paged_decode_attn)."""
+        d = self.desc
+        qp = self._check(q, (d.batch, d.n_heads, d.head_dim), name="q")
+        op = self._check(out, (d.batch, d.n_heads, d.head_dim), name="out")
+        if sm_scale is None:
+            raise ValueError("sm_scale is required")
+        _call("kvc_paged_decode_attn", self.handle, layer, qp, op, self._table(block_table),
+              self._idx(valid_lens, "valid_lens"), self._idx(cache_index, "cache_index"), float(sm_scale),
+              _stream(self.device))
 
 
 def _memcpy_d2d(dst, src, nbytes, device):

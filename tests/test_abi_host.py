@@ -122,3 +122,44 @@ def test_host_only_calls_reject_null_handles(lib):
     assert lib.kvc_free(None) == kvc.KVC_OK
     for s in range(7):
         assert lib.kvc_strerror(s)
+
+
+@pytest.mark.parametrize("shape", [
+    (1, 2, 8, 2, 128, 64, 16, 9),        # small: 9 blocks of 16 rows
+    (32, 16, 32, 8, 128, 4096, 16, 4096),  # Llama-3-8B-shaped, 4096 blocks of 16
+    (2, 1, 4, 4, 64, 1024, 256, 5),       # largest block size
+])
+def test_kvc_bytes_paged_matches_pool_model(lib, shape):
+    """Block-table cache bytes equal the oracle pool's size: [L][2][num_blocks][H_kv][block_size][D] bf16."""
+    from oracle.paged import RefPagedCache
+    L, B, H, Hkv, D, S, bs, nb = shape
+    got = kvc.paged_cache_bytes(kvc.gqa_desc(L, B, H, Hkv, D, S, "bf16"), bs, nb)
+    assert got == 2 * L * nb * Hkv * bs * D * 2
+    if L * nb * bs <= 1 << 16:
+        assert got == RefPagedCache(L, nb, Hkv, bs, D, "bf16", S).pool.nbytes
+
+
+@pytest.mark.parametrize("desc,bs,nb,status", [
+    (kvc.gqa_desc(1, 2, 8, 2, 128, 64, "bf16"), 24, 8, kvc.KVC_ERR_INVALID_ARG),   # 64 % 24 != 0
+    (kvc.gqa_desc(1, 2, 8, 2, 128, 64, "bf16"), 0, 8, kvc.KVC_ERR_INVALID_ARG),
+    (kvc.gqa_desc(1, 2, 8, 2, 128, 64, "bf16"), 16, 0, kvc.KVC_ERR_INVALID_ARG),
+    (kvc.gqa_desc(1, 2, 8, 2, 128, 64, "bf16"), 8, 8, kvc.KVC_ERR_UNSUPPORTED),    # tiles span <= 2 blocks
+    (kvc.gqa_desc(1, 2, 8, 2, 128, 96, "bf16"), 48, 8, kvc.KVC_ERR_UNSUPPORTED),   # not a power of two
+    (kvc.gqa_desc(1, 2, 8, 2, 128, 1024, "bf16"), 512, 8, kvc.KVC_ERR_UNSUPPORTED),
+    (kvc.gqa_desc(1, 2, 8, 2, 128, 16 * 4097, "bf16"), 16, 8, kvc.KVC_ERR_UNSUPPORTED),  # table > 4096
+    (kvc.gqa_desc(1, 2, 8, 8, 128, 64, "bf16"), 16, 1 << 16, kvc.KVC_ERR_UNSUPPORTED),   # pool >= 2^30
+    (kvc.gqa_desc(1, 2, 8, 2, 128, 64, "f32"), 16, 8, kvc.KVC_ERR_UNSUPPORTED),
+    (kvc.gqa_desc(1, 2, 8, 2, 128, 64, "i8"), 16, 8, kvc.KVC_ERR_UNSUPPORTED),
+    (kvc.mla_desc(1, 2, 16, 64), 16, 8, kvc.KVC_ERR_UNSUPPORTED),
+], ids=["ragged", "bs0", "nb0", "bs8", "bs48", "bs512", "wide_table", "big_pool", "f32", "i8", "latent"])
+def test_kvc_bytes_paged_rejects(lib, desc, bs, nb, status):
+    out = ctypes.c_uint64(0)
+    assert lib.kvc_bytes_paged(ctypes.byref(desc), bs, nb, ctypes.byref(out)) == status
+
+
+def test_paged_calls_reject_null_handles(lib):
+    z = ctypes.c_void_p(16)
+    assert lib.kvc_paged_append(None, 0, z, z, z, z, 1, None) == kvc.KVC_ERR_INVALID_ARG
+    assert lib.kvc_paged_decode_attn(None, 0, z, z, z, z, z, ctypes.c_float(0.1), None) == kvc.KVC_ERR_INVALID_ARG
+    assert lib.kvc_bytes_paged(None, 16, 4, ctypes.byref(ctypes.c_uint64())) == kvc.KVC_ERR_INVALID_ARG
+    assert lib.kvc_alloc_paged(None, 16, 4, None, None) == kvc.KVC_ERR_INVALID_ARG
