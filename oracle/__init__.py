@@ -14,10 +14,11 @@ Everything here follows the four web pages on the subject directly:
   per-token growth equation.
 * "KV Cache Optimization: GQA Audit, In-Place Buffers, Persistent Prompts"
   -- the ``[B, nKvHeads, T, headDim]`` layout, in-place slice-assign append,
-  reads sliced to the valid length, byte examples.
+  reads sliced to the valid length, byte examples, saving the live prefix.
 * "10.3 - KV cache implementation details" -- the exact byte formula and
   its variants (MQA, GQA, MLA, quantised), the decode loop (append, then
-  single-query softmax attention over the cache).
+  single-query softmax attention over the cache), block tables and shared
+  prefixes.
 
 Modules
 -------
@@ -27,6 +28,8 @@ buffer        bit-exact model of the static cache buffer and its append
 attention     decode attention (plain definition) and no-cache causal attention
 mla           latent (MLA) decode, materialised and absorbed forms
 quant         int8 storage with a float32 scale per row: codes, dequantisation, the cache model
+paged         block-table layout: pools of fixed-size blocks, append and gather through tables
+persist       the live-prefix image: save (pack) and load (unpack, shared prefixes)
 
 Parity status: every function here has a pin in ``tests/test_oracle_*.py``
 (printed worked examples, closed forms, invariants, library routines);
