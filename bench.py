@@ -19,8 +19,10 @@ Reported (one JSON line on stdout):
   cpu_baseline the float64 oracle timed on a bounded sample on the host
   mla, i8,     side legs (not the headline): latent (MLA) attention, the same
   prefill,     Llama-3-shaped stack on an int8 cache (codes + row scales), the
-  paged        causal prefill of one 4096-token prompt, and the same stack on a
-               block-table cache of 16-row blocks scattered over the pool
+  paged,       causal prefill of one 4096-token prompt, the same stack on a
+  prefix       block-table cache of 16-row blocks scattered over the pool, and
+               saving / loading the live prefix (the batch's, and one prompt's
+               from device and from pinned host memory)
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -61,6 +63,7 @@ def parse():
     p.add_argument("--no-i8", action="store_true", help="skip the int8-cache leg")
     p.add_argument("--no-prefill", action="store_true", help="skip the prefill leg")
     p.add_argument("--no-paged", action="store_true", help="skip the block-table cache leg")
+    p.add_argument("--no-prefix", action="store_true", help="skip the prefix save/load leg")
     p.add_argument("--mla-workgroups", type=int, default=0,
                    help="force the latent leg's persistent grid size (0 = device default)")
     p.add_argument("--workgroups", type=int, default=0,
@@ -127,7 +130,7 @@ class Workload:
         self.decode_alg_bytes = (self.kv_read_per_layer + 2 * B * H * D * p + 8 * B)
         self.append_bytes = 2 * (2 * B * Hkv * D * p)   # read + write of the new K and V rows
         self.fused_alg_bytes = self.decode_alg_bytes + self.append_bytes
-        self.kernel_name = (f"gqa_decode_kernel<MfmaPiece<{D}>> (bf16 MFMA piece, d_h={D}), "
+        self.kernel_name = (f"gqa_decode_kernel<MfmaPiece<{D}, false>> (bf16 MFMA piece, d_h={D}), "
                             f"launched by kvc_append_decode_attn")
 
     def layer_step(self, layer, ev=None):
@@ -463,6 +466,72 @@ def bench_prefill(torch, steps, warmup):
                 step="kvc_prefill_attn: write the prompt rows into the cache + causal attention, per layer")
 
 
+def bench_prefix(torch, wl, reps, prefill):
+    """Saving and loading the live prefix (kvc_save_prefix / kvc_load_prefix): the Llama-3-8B-shaped
+    32-layer batch through a device-resident image, and one 4096-token prompt's 32 layers (B=1) from
+    device memory and from pinned host memory, which a later run loads in place of its prefill.
+    Both calls synchronise their stream, so each is timed by the host clock around the call; GB/s is
+    payload bytes per second in each direction (the copy reads and writes that many bytes)."""
+    import time
+    from static_kv_cache_amd import kvc, synthetic
+    dev = torch.device("cuda:0")
+
+    def timed(fn):
+        fn()
+        ts = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+        return float(np.median(ts)) * 1e3
+
+    lens = wl.host["valid_lens"]
+    nbytes = wl.cache.prefix_bytes(lens)
+    img = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    save_ms = timed(lambda: wl.cache.save_prefix(lens, img))
+    load_ms = timed(lambda: wl.cache.load_prefix(img))
+    wl.cache.check()
+    payload = wl.L * wl.sum_valid * 2 * wl.Hkv * wl.D * 2
+    del img
+    log(f"bench: prefix save {save_ms:.3f} ms, load {load_ms:.3f} ms for {payload / 1e9:.2f} GB "
+        f"({payload / (save_ms * 1e-3) / 1e9:.0f} / {payload / (load_ms * 1e-3) / 1e9:.0f} GB/s)")
+
+    # one 4096-token prompt, 32 layers
+    L, H, Hkv, D, T = wl.L, wl.H, wl.Hkv, wl.D, wl.S
+    one = kvc.Cache(kvc.gqa_desc(L, 1, H, Hkv, D, T, "bf16"))
+    rng = np.random.default_rng(17)
+    k = kvc.to_device(synthetic.draw(rng, (1, Hkv, T, D), "bf16"), dev)
+    v = kvc.to_device(synthetic.draw(rng, (1, Hkv, T, D), "bf16"), dev)
+    for layer in range(L):
+        one.prefill_fill(layer, k, v, 0)
+    del k, v
+    plen = [T]
+    pbytes = one.prefix_bytes(plen)
+    pimg = torch.empty(pbytes, dtype=torch.uint8, device=dev)
+    host = torch.empty(pbytes, dtype=torch.uint8).pin_memory()
+    p_save_ms = timed(lambda: one.save_prefix(plen, pimg))
+    p_load_ms = timed(lambda: one.load_prefix(pimg))
+    h_save_ms = timed(lambda: one.save_prefix(plen, host))
+    h_load_ms = timed(lambda: one.load_prefix(host))
+    one.check()
+    one.free()
+    ppay = L * T * 2 * Hkv * D * 2
+    log(f"bench: prompt prefix ({ppay / 1e6:.0f} MB): device load {p_load_ms:.3f} ms, pinned-host load "
+        f"{h_load_ms:.3f} ms")
+    res = dict(workload="llama3_8b_gqa_bf16 batch prefix, and one 4096-token prompt (B=1), 32 layers",
+               batch_payload_bytes=payload, batch_save_ms=round(save_ms, 3), batch_load_ms=round(load_ms, 3),
+               batch_save_gbs=round(payload / (save_ms * 1e-3) / 1e9, 1),
+               batch_load_gbs=round(payload / (load_ms * 1e-3) / 1e9, 1),
+               prompt_payload_bytes=ppay, prompt_device_save_ms=round(p_save_ms, 3),
+               prompt_device_load_ms=round(p_load_ms, 3), prompt_host_save_ms=round(h_save_ms, 3),
+               prompt_host_load_ms=round(h_load_ms, 3),
+               prompt_host_load_gbs=round(ppay / (h_load_ms * 1e-3) / 1e9, 1),
+               timing=f"host clock around each synchronous call, median of {reps}")
+    if prefill is not None:
+        res["prompt_prefill_attention_ms_32_layers"] = prefill["ttft_attention_ms_32_layers"]
+    return res
+
+
 def time_steps(torch, fn, steps):
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -598,10 +667,11 @@ def main():
                 decode_only_us=round(decode_ms * 1e3, 3),
                 decode_only_achieved=round(wl.decode_alg_bytes / (decode_ms * 1e-3) / 1e9, 2))
     wg_forced = wl.cache.workgroups()[0]
+    prefill = None if args.no_prefill else bench_prefill(torch, max(3, args.steps // 10), 1)
+    prefix = None if args.no_prefix else bench_prefix(torch, wl, 5, prefill)
     wl.cache.free()
     mla = None if args.no_mla else bench_mla(torch, max(5, args.steps // 2), 2, args.mla_workgroups)
     i8 = None if args.no_i8 else bench_i8(torch, max(5, args.steps // 2), 2, decode_ms * 1e3)
-    prefill = None if args.no_prefill else bench_prefill(torch, max(3, args.steps // 10), 1)
     paged = None if args.no_paged else bench_paged(torch, max(5, args.steps // 2), 2, decode_ms * 1e3)
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl, args.cpu_repeats)
     line = {
@@ -634,6 +704,7 @@ def main():
         "i8": i8,
         "prefill": prefill,
         "paged": paged,
+        "prefix": prefix,
     }
     print(json.dumps(line), flush=True)
 

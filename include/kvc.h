@@ -285,6 +285,51 @@ kvc_status kvc_paged_decode_attn(kvc_cache* cache, int32_t layer, const void* q,
                                  const int32_t* block_table, const int32_t* valid_lens,
                                  const int32_t* cache_index, float sm_scale, void* stream);
 
+/* ---- live-prefix save and load -------------------------------------------
+ * "KV Cache Optimization: GQA Audit, In-Place Buffers, Persistent Prompts",
+ * "#3 Persistent KV across sessions" and its file map: the cache after a
+ * prompt's prefill is saved once and loaded by later runs, which skip the
+ * prefill with identical output; a pre-allocated cache saves only its live
+ * prefix, and a load sets the valid lengths from what was saved. "10.3 - KV
+ * cache implementation details", section 7.3: requests sharing a prefix
+ * reuse its K/V.
+ *
+ * Image (little-endian, version 1):
+ *   header: int32 [magic 0x3143564B ("KVC1"), version 1, the ten kvc_desc
+ *     fields in declaration order, header bytes, 0] (56 bytes), the payload
+ *     bytes as uint64 at byte 56, the batch's valid lengths as int32 from
+ *     byte 64, zero padding to a multiple of 256 bytes;
+ *   payload: for each layer, K then V (the latent cache: its one tensor), for
+ *     each sequence, for each kv head, rows [0, n_b) as stored; for an int8
+ *     cache all codes first, then the float32 row scales in the same order.
+ * The payload is kvc_logical_bytes of the lengths. File I/O, naming and
+ * invalidation are the caller's. Block-table caches are not supported
+ * (KVC_ERR_INVALID_ARG). Both calls are ordered on `stream` and synchronise
+ * it before returning. */
+
+/* Image bytes for host_valid_lens[B] (each in [0, max_context], else
+ * KVC_ERR_CAPACITY). Pure host. */
+kvc_status kvc_prefix_bytes(const kvc_cache* cache, const int32_t* host_valid_lens, uint64_t* bytes);
+
+/* Write the image of rows [0, n_b) of every layer and sequence, n_b =
+ * host_valid_lens[b], to dst: device memory or pinned host memory of
+ * dst_bytes >= kvc_prefix_bytes (else KVC_ERR_INVALID_ARG). */
+kvc_status kvc_save_prefix(kvc_cache* cache, const int32_t* host_valid_lens, void* dst, uint64_t dst_bytes,
+                           void* stream);
+
+/* Load an image of src_bytes (device or pinned host memory): saved sequence
+ * host_src_seq[b] (in [0, saved batch), or -1 to leave b alone) is written
+ * into rows [0, n) of sequence b, n being its saved length, and
+ * host_valid_lens[b] is set to n (left as it is for -1). Several b may name
+ * one saved sequence (a shared prefix). Rows at or past n are not touched.
+ * The image must come from a cache with the same attention kind, dtype,
+ * n_layers, n_kv_heads, head_dim, latent_dim and rope_dim; batch, n_heads
+ * and max_context may differ. A malformed or mismatched image, or a bad
+ * host_src_seq entry, gives KVC_ERR_INVALID_ARG, and a saved length above
+ * this cache's max_context KVC_ERR_CAPACITY; nothing is written then. */
+kvc_status kvc_load_prefix(kvc_cache* cache, const void* src, uint64_t src_bytes, const int32_t* host_src_seq,
+                           int32_t* host_valid_lens, void* stream);
+
 /* Force the number of persistent workgroups attention launches (0 restores
  * the default: one per compute unit). The rows of
  * all sequences and kv heads are divided evenly among them, so this only

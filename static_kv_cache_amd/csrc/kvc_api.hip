@@ -155,6 +155,58 @@ uint64_t paged_bytes(const kvc_desc* d, int32_t block_size, int32_t num_blocks) 
 kvc_status alloc_impl(const kvc_desc* desc, void* external, uint64_t bytes, int32_t block_size,
                       int32_t num_blocks, kvc_cache** out);
 
+// Stored bytes of one cached row position over all of a layer's tensors
+// (K and V of every kv head, plus int8 row scales; the latent row).
+uint64_t bytes_per_position(const kvc_cache* c) {
+  uint64_t per_row = c->d.attn == KVC_ATTN_GQA ? 2ull * c->d.n_kv_heads * c->d.head_dim * c->elem
+                                               : (uint64_t)c->row_elems * c->elem;
+  if (c->d.dtype == KVC_I8) per_row += 2ull * c->d.n_kv_heads * sizeof(float);
+  return per_row;
+}
+
+// ---- live-prefix image ("KV Cache Optimization ...", "#3 Persistent KV
+// across sessions"; layout in include/kvc.h) -----------------------------
+constexpr int32_t kImageMagic = 0x3143564B;  // "KVC1"
+constexpr int32_t kImageVersion = 1;
+
+uint64_t image_header_bytes(int batch) { return ((uint64_t)4 * (16 + batch) + 255) / 256 * 256; }
+
+// The header for `lens` (batch entries) of cache c.
+void image_header(const kvc_cache* c, const int32_t* lens, uint64_t payload, unsigned char* out) {
+  const uint64_t hb = image_header_bytes(c->d.batch);
+  memset(out, 0, hb);
+  const int32_t w[14] = {kImageMagic, kImageVersion, c->d.attn, c->d.dtype, c->d.n_layers, c->d.batch,
+                         c->d.n_heads, c->d.n_kv_heads, c->d.head_dim, c->d.max_context, c->d.latent_dim,
+                         c->d.rope_dim, (int32_t)hb, 0};
+  memcpy(out, w, sizeof(w));
+  memcpy(out + 56, &payload, 8);
+  memcpy(out + 64, lens, (size_t)c->d.batch * 4);
+}
+
+// One direction of the payload copy for the sequences' runs in `map_host`
+// ([B][2]: rows, first image row); total_rows = rows of all saved sequences.
+hipError_t prefix_copy(kvc_cache* c, uint8_t* payload, const int32_t* map_host, bool save, int64_t total_rows,
+                       hipStream_t s) {
+  int max_rows = 0;
+  for (int b = 0; b < c->d.batch; ++b) max_rows = map_host[2 * b] > max_rows ? map_host[2 * b] : max_rows;
+  hipError_t e = hipMemcpyAsync(c->ws_map, map_host, (size_t)c->d.batch * 2 * sizeof(int32_t),
+                                hipMemcpyHostToDevice, s);
+  if (e != hipSuccess || max_rows == 0) return e;
+  const bool gqa = c->d.attn == KVC_ATTN_GQA;
+  const int kv_parts = gqa ? 2 : 1;
+  const int groups = gqa ? c->d.n_kv_heads : 1;
+  const int row_bytes = c->row_elems * c->elem;
+  e = kvc_launch_prefix_copy(c->base, payload, c->ws_map, save, c->layer_bytes, c->kv_bytes, c->d.n_layers,
+                             kv_parts, c->d.batch, max_rows, groups, c->d.max_context, row_bytes, 16, total_rows, s);
+  if (e == hipSuccess && c->d.dtype == KVC_I8) {
+    const uint64_t codes = (uint64_t)c->d.n_layers * kv_parts * total_rows * groups * row_bytes;
+    e = kvc_launch_prefix_copy(c->scales, payload + codes, c->ws_map, save, c->scale_layer_bytes,
+                               c->scale_kv_bytes, c->d.n_layers, kv_parts, c->d.batch, max_rows, groups,
+                               c->d.max_context, 4, 4, total_rows, s);
+  }
+  return e;
+}
+
 }  // namespace
 
 extern "C" {
@@ -257,6 +309,7 @@ kvc_status alloc_impl(const kvc_desc* desc, void* external, uint64_t bytes, int3
   const uint64_t cnt_bytes = (uint64_t)desc->batch * desc->n_heads * sizeof(int32_t);
   if (ok) ok = hipMalloc((void**)&c->ws_cnt, cnt_bytes) == hipSuccess;
   if (ok) ok = hipMemset(c->ws_cnt, 0, cnt_bytes) == hipSuccess;
+  if (ok) ok = hipMalloc((void**)&c->ws_map, (uint64_t)desc->batch * 2 * sizeof(int32_t)) == hipSuccess;
   if (ok) ok = hipMalloc((void**)&c->err_flag, 256) == hipSuccess;
   if (ok) ok = hipMemset(c->err_flag, 0, 256) == hipSuccess;
   if (ok && desc->attn == KVC_ATTN_MLA) {
@@ -286,6 +339,7 @@ kvc_status kvc_free(kvc_cache* c) {
   if (c->ws_ml) (void)hipFree(c->ws_ml);
   if (c->ws_cnt) (void)hipFree(c->ws_cnt);
   if (c->err_flag) (void)hipFree(c->err_flag);
+  if (c->ws_map) (void)hipFree(c->ws_map);
   if (c->ws_qabs) (void)hipFree(c->ws_qabs);
   if (c->ws_olat) (void)hipFree(c->ws_olat);
   delete c;
@@ -315,11 +369,109 @@ kvc_status kvc_logical_bytes(const kvc_cache* c, const int32_t* host_valid_lens,
     if (host_valid_lens[b] < 0 || host_valid_lens[b] > c->d.max_context) return KVC_ERR_CAPACITY;
     total += (uint64_t)host_valid_lens[b];
   }
-  uint64_t per_row = c->d.attn == KVC_ATTN_GQA ? 2ull * c->d.n_kv_heads * c->d.head_dim * c->elem
-                                               : (uint64_t)c->row_elems * c->elem;
-  if (c->d.dtype == KVC_I8) per_row += 2ull * c->d.n_kv_heads * sizeof(float);  // the rows' scales
-  *out = (uint64_t)c->d.n_layers * per_row * total;
+  *out = (uint64_t)c->d.n_layers * bytes_per_position(c) * total;
   return KVC_OK;
+}
+
+kvc_status kvc_prefix_bytes(const kvc_cache* c, const int32_t* host_valid_lens, uint64_t* bytes) {
+  if (!c || c->paged || !bytes) return KVC_ERR_INVALID_ARG;
+  uint64_t payload = 0;
+  kvc_status st = kvc_logical_bytes(c, host_valid_lens, &payload);
+  if (st != KVC_OK) return st;
+  *bytes = image_header_bytes(c->d.batch) + payload;
+  return KVC_OK;
+}
+
+kvc_status kvc_save_prefix(kvc_cache* c, const int32_t* host_valid_lens, void* dst, uint64_t dst_bytes,
+                           void* stream) {
+  if (!c || c->paged || !dst || ((uintptr_t)dst % 16) != 0) return KVC_ERR_INVALID_ARG;
+  uint64_t need = 0;
+  kvc_status st = kvc_prefix_bytes(c, host_valid_lens, &need);
+  if (st != KVC_OK) return st;
+  if (dst_bytes < need) return KVC_ERR_INVALID_ARG;
+  const uint64_t hb = image_header_bytes(c->d.batch);
+  unsigned char* hdr = (unsigned char*)malloc(hb);
+  int32_t* map = (int32_t*)malloc((size_t)c->d.batch * 2 * sizeof(int32_t));
+  if (!hdr || !map) { free(hdr); free(map); return KVC_ERR_OOM; }
+  int64_t rows = 0;
+  for (int b = 0; b < c->d.batch; ++b) {
+    map[2 * b] = host_valid_lens[b];
+    map[2 * b + 1] = (int32_t)rows;
+    rows += host_valid_lens[b];
+  }
+  image_header(c, host_valid_lens, need - hb, hdr);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(dst, hdr, hb, hipMemcpyDefault, s);
+  if (e == hipSuccess) e = prefix_copy(c, (uint8_t*)dst + hb, map, true, rows, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  free(hdr);
+  free(map);
+  return e == hipSuccess ? KVC_OK : KVC_ERR_DEVICE;
+}
+
+kvc_status kvc_load_prefix(kvc_cache* c, const void* src, uint64_t src_bytes, const int32_t* host_src_seq,
+                           int32_t* host_valid_lens, void* stream) {
+  if (!c || c->paged || !src || ((uintptr_t)src % 16) != 0 || !host_src_seq || !host_valid_lens)
+    return KVC_ERR_INVALID_ARG;
+  if (src_bytes < 64) return KVC_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  unsigned char head[64];
+  if (hipMemcpyAsync(head, src, 64, hipMemcpyDefault, s) != hipSuccess || hipStreamSynchronize(s) != hipSuccess)
+    return KVC_ERR_DEVICE;
+  int32_t w[14];
+  uint64_t payload = 0;
+  memcpy(w, head, sizeof(w));
+  memcpy(&payload, head + 56, 8);
+  // the image's descriptor: the same cache rows, any batch / query heads / capacity
+  const kvc_desc& d = c->d;
+  if (w[0] != kImageMagic || w[1] != kImageVersion) return KVC_ERR_INVALID_ARG;
+  if (w[2] != d.attn || w[3] != d.dtype || w[4] != d.n_layers || w[7] != d.n_kv_heads || w[8] != d.head_dim ||
+      w[10] != d.latent_dim || w[11] != d.rope_dim)
+    return KVC_ERR_INVALID_ARG;
+  const int src_batch = w[5];
+  const int src_context = w[9];
+  if (src_batch < 1 || src_batch > KVC_MAX_BATCH || src_context < 1) return KVC_ERR_INVALID_ARG;
+  const uint64_t hb = image_header_bytes(src_batch);
+  if ((uint64_t)w[12] != hb || w[13] != 0 || src_bytes < hb) return KVC_ERR_INVALID_ARG;
+  int32_t* lens = (int32_t*)malloc((size_t)src_batch * sizeof(int32_t));
+  int32_t* map = (int32_t*)malloc((size_t)d.batch * 2 * sizeof(int32_t));
+  int64_t* first = (int64_t*)malloc((size_t)src_batch * sizeof(int64_t));
+  kvc_status st = (lens && map && first) ? KVC_OK : KVC_ERR_OOM;
+  int64_t rows = 0;
+  if (st == KVC_OK &&
+      (hipMemcpyAsync(lens, (const unsigned char*)src + 64, (size_t)src_batch * 4, hipMemcpyDefault, s) !=
+           hipSuccess ||
+       hipStreamSynchronize(s) != hipSuccess))
+    st = KVC_ERR_DEVICE;
+  for (int i = 0; st == KVC_OK && i < src_batch; ++i) {
+    if (lens[i] < 0 || lens[i] > src_context) st = KVC_ERR_INVALID_ARG;
+    first[i] = rows;
+    rows += lens[i];
+  }
+  if (st == KVC_OK) {
+    // the payload must be exactly the saved rows, and present
+    const uint64_t want = (uint64_t)d.n_layers * bytes_per_position(c) * (uint64_t)rows;
+    if (payload != want || src_bytes - hb < payload || rows > 0x7fffffffLL) st = KVC_ERR_INVALID_ARG;
+  }
+  for (int b = 0; st == KVC_OK && b < d.batch; ++b) {
+    const int32_t sq = host_src_seq[b];
+    if (sq < -1 || sq >= src_batch) { st = KVC_ERR_INVALID_ARG; break; }
+    map[2 * b] = sq < 0 ? 0 : lens[sq];
+    map[2 * b + 1] = sq < 0 ? 0 : (int32_t)first[sq];
+    if (map[2 * b] > d.max_context) st = KVC_ERR_CAPACITY;
+  }
+  if (st == KVC_OK) {
+    hipError_t e = prefix_copy(c, (uint8_t*)const_cast<void*>(src) + hb, map, false, rows, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) st = KVC_ERR_DEVICE;
+  }
+  if (st == KVC_OK)
+    for (int b = 0; b < d.batch; ++b)
+      if (host_src_seq[b] >= 0) host_valid_lens[b] = lens[host_src_seq[b]];
+  free(lens);
+  free(map);
+  free(first);
+  return st;
 }
 
 kvc_status kvc_prefill_fill(kvc_cache* c, int32_t layer, const void* k, const void* v, int32_t start,

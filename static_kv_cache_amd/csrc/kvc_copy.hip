@@ -84,7 +84,65 @@ __global__ __launch_bounds__(256) void paged_rows_kernel(
   pool_v[dst] = src_v[src];
 }
 
+// Live-prefix image ("KV Cache Optimization: GQA Audit, In-Place Buffers,
+// Persistent Prompts", "#3 Persistent KV across sessions": only the live
+// prefix is saved). Grid (x chunks, sequence b, layer * kv_parts + kv): the
+// n_b rows of every kv head of (b, layer, kv) are one run in the cache per
+// head ([S] rows apart) and one packed run in the image, copied as units of
+// U (16-byte vectors for rows, 4-byte words for int8 scales).
+template <typename U>
+__global__ __launch_bounds__(256) void prefix_copy_kernel(U* __restrict__ cache, U* __restrict__ image,
+                                                          const int32_t* __restrict__ map, bool save,
+                                                          long long layer_units, long long kv_units, int kv_parts,
+                                                          int groups, int max_context, int row_units,
+                                                          long long total_rows) {
+  const int b = blockIdx.y;
+  const int lk = blockIdx.z;
+  const int n = map[2 * b];
+  if (n <= 0) return;
+  const long long first = map[2 * b + 1];
+  const int layer = lk / kv_parts;
+  const int kv = lk - layer * kv_parts;
+  const long long run = (long long)n * row_units;  // units of one kv head's rows
+  const long long units = run * groups;
+  U* cb = cache + layer * layer_units + kv * kv_units + (long long)b * groups * max_context * row_units;
+  U* ib = image + ((long long)lk * total_rows + first) * groups * row_units;
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < units; i += (long long)gridDim.x * 256) {
+    const int g = (int)(i / run);
+    const long long rem = i - g * run;
+    U* cp = cb + (long long)g * max_context * row_units + rem;
+    U* ip = ib + g * run + rem;
+    if (save) *ip = *cp; else *cp = *ip;
+  }
+}
+
 }  // namespace
+
+hipError_t kvc_launch_prefix_copy(uint8_t* cache, uint8_t* image, const int32_t* map, bool save,
+                                  uint64_t layer_bytes, uint64_t kv_bytes, int n_layers, int kv_parts, int batch,
+                                  int max_batch_rows, int groups, int max_context, int row_bytes, int unit_bytes,
+                                  int64_t total_rows, hipStream_t stream) {
+  if (row_bytes % unit_bytes != 0 || layer_bytes % unit_bytes != 0 || kv_bytes % unit_bytes != 0)
+    return hipErrorInvalidValue;
+  if (max_batch_rows <= 0) return hipSuccess;  // no rows to copy
+  if (batch > 65535 || (long long)n_layers * kv_parts > 65535) return hipErrorInvalidValue;
+  const int row_units = row_bytes / unit_bytes;
+  const long long units = (long long)max_batch_rows * groups * row_units;
+  long long gx = (units + 1023) / 1024;  // about four units per thread
+  if (gx > 65535) gx = 65535;
+  const dim3 grid((unsigned)gx, (unsigned)batch, (unsigned)(n_layers * kv_parts));
+  if (unit_bytes == 16)
+    prefix_copy_kernel<uint4><<<grid, dim3(256), 0, stream>>>(
+        (uint4*)cache, (uint4*)image, map, save, (long long)(layer_bytes / 16), (long long)(kv_bytes / 16), kv_parts,
+        groups, max_context, row_units, total_rows);
+  else if (unit_bytes == 4)
+    prefix_copy_kernel<uint32_t><<<grid, dim3(256), 0, stream>>>(
+        (uint32_t*)cache, (uint32_t*)image, map, save, (long long)(layer_bytes / 4), (long long)(kv_bytes / 4),
+        kv_parts, groups, max_context, row_units, total_rows);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
 
 hipError_t kvc_launch_paged_rows(const void* src_k, const void* src_v, uint8_t* pool_k, uint8_t* pool_v,
                                  const int32_t* table, int batch, int n_kv_heads, int t, int row_bytes,

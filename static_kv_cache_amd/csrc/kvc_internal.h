@@ -27,6 +27,7 @@ struct kvc_cache {
   uint64_t scale_layer_bytes;  // int8: bytes of one layer's K and V scales (0 otherwise)
   uint64_t scale_kv_bytes;     // int8: offset of the V scales from the K scales in a layer
   uint8_t* scales;        // int8: [L][2][B][H_kv][S] float32 scales (after the codes), else NULL
+  int32_t* ws_map;        // [B][2]: rows and first image row of each sequence's run (prefix save/load)
   bool paged;             // block-table cache: layer = [K|V][num_blocks][H_kv][block_size][d_h]
   int block_size, block_shift, num_blocks, table_width;  // table_width = max_context / block_size
 
@@ -65,6 +66,15 @@ hipError_t kvc_launch_paged_rows(const void* src_k, const void* src_v, uint8_t* 
                                  const int32_t* table, int batch, int n_kv_heads, int t, int row_bytes,
                                  int block_shift, int num_blocks, int table_width, int max_context,
                                  const int32_t* dev_start, int32_t* err_flag, hipStream_t stream);
+
+// Live-prefix copy between the cache and an image payload (save: cache ->
+// image, load: image -> cache). map[2b] rows of sequence b (<= 0: nothing),
+// starting at image row map[2b + 1] of each (layer, K|V) section of
+// total_rows * n_kv_heads rows. unit_bytes is 16 (rows) or 4 (int8 scales).
+hipError_t kvc_launch_prefix_copy(uint8_t* cache, uint8_t* image, const int32_t* map, bool save,
+                                  uint64_t layer_bytes, uint64_t kv_bytes, int n_layers, int kv_parts, int batch,
+                                  int max_batch_rows, int groups, int max_context, int row_bytes, int unit_bytes,
+                                  int64_t total_rows, hipStream_t stream);
 
 // Quantising row copy into an int8 cache: as kvc_launch_copy_rows for bf16
 // source rows [B][H_kv][t][d] (d = head_dim), writing each row's int8 codes

@@ -61,6 +61,9 @@ _SIGS = {
     "kvc_alloc_paged": [ctypes.POINTER(Desc), _i32, _i32, _p, ctypes.POINTER(_p)],
     "kvc_paged_append": [_p, _i32, _p, _p, _p, _p, _i32, _p],
     "kvc_paged_decode_attn": [_p, _i32, _p, _p, _p, _p, _p, ctypes.c_float, _p],
+    "kvc_prefix_bytes": [_p, _p, ctypes.POINTER(ctypes.c_uint64)],
+    "kvc_save_prefix": [_p, _p, _p, ctypes.c_uint64, _p],
+    "kvc_load_prefix": [_p, _p, ctypes.c_uint64, _p, _p, _p],
     "kvc_set_workgroups": [_p, _i32],
     "kvc_get_workgroups": [_p, ctypes.POINTER(_i32), ctypes.POINTER(_i32)],
     "kvc_check": [_p, _p],
@@ -327,6 +330,55 @@ class Cache:
             raise ValueError("sm_scale is required")
         _call("kvc_mla_decode", self.handle, layer, *args, self._idx(valid_lens, "valid_lens"),
               self._idx(cache_index, "cache_index"), float(sm_scale), _stream(self.device))
+
+    # -- live-prefix image (kvc_prefix_bytes / kvc_save_prefix / kvc_load_prefix) --
+    def _host_lens(self, valid_lens):
+        v = np.ascontiguousarray(valid_lens, dtype=np.int32)
+        if v.shape != (self.desc.batch,):
+            raise ValueError("valid_lens must have shape [B]")
+        return v
+
+    def _image_ptr(self, image):
+        torch = _torch()
+        if image.dtype != torch.uint8 or image.dim() != 1 or not image.is_contiguous():
+            raise ValueError("image must be a contiguous 1-D uint8 tensor")
+        if image.device.type == "cpu" and not image.is_pinned():
+            raise ValueError("a host image must be pinned memory")
+        if image.device.type != "cpu" and image.device != self.device:
+            raise ValueError(f"image must be on {self.device} or pinned host memory")
+        if image.data_ptr() % 16 != 0:
+            raise ValueError("image must be 16-byte aligned")
+        return ctypes.c_void_p(image.data_ptr()), image.numel()
+
+    def prefix_bytes(self, valid_lens):
+        v = self._host_lens(valid_lens)
+        out = ctypes.c_uint64(0)
+        _call("kvc_prefix_bytes", self.handle, v.ctypes.data_as(ctypes.c_void_p), ctypes.byref(out))
+        return out.value
+
+    def save_prefix(self, valid_lens, dst=None):
+        """Image of rows [0, valid_lens[b]) of every layer and sequence (kvc_save_prefix), as a uint8
+        tensor: `dst` if given (device or pinned host), else a new device tensor."""
+        torch = _torch()
+        v = self._host_lens(valid_lens)
+        n = self.prefix_bytes(v)
+        if dst is None:
+            dst = torch.empty(n, dtype=torch.uint8, device=self.device)
+        ptr, size = self._image_ptr(dst)
+        _call("kvc_save_prefix", self.handle, v.ctypes.data_as(ctypes.c_void_p), ptr, size, _stream(self.device))
+        return dst
+
+    def load_prefix(self, image, src_seq=None, valid_lens=None):
+        """Load an image (kvc_load_prefix): sequence b gets saved sequence src_seq[b] (-1: untouched;
+        default b -> b). Returns the valid lengths: the loaded ones, and valid_lens[b] (default -1)
+        where src_seq[b] = -1."""
+        B = self.desc.batch
+        src = np.arange(B, dtype=np.int32) if src_seq is None else self._host_lens(src_seq)
+        lens = np.full(B, -1, dtype=np.int32) if valid_lens is None else self._host_lens(valid_lens).copy()
+        ptr, size = self._image_ptr(image)
+        _call("kvc_load_prefix", self.handle, ptr, size, src.ctypes.data_as(ctypes.c_void_p),
+              lens.ctypes.data_as(ctypes.c_void_p), _stream(self.device))
+        return lens
 
     def set_workgroups(self, n):
         """Force the persistent attention grid size (0 = device default)."""

@@ -163,3 +163,12 @@ def test_paged_calls_reject_null_handles(lib):
     assert lib.kvc_paged_decode_attn(None, 0, z, z, z, z, z, ctypes.c_float(0.1), None) == kvc.KVC_ERR_INVALID_ARG
     assert lib.kvc_bytes_paged(None, 16, 4, ctypes.byref(ctypes.c_uint64())) == kvc.KVC_ERR_INVALID_ARG
     assert lib.kvc_alloc_paged(None, 16, 4, None, None) == kvc.KVC_ERR_INVALID_ARG
+
+
+def test_prefix_calls_reject_null_handles(lib):
+    z = ctypes.c_void_p(16)
+    n = ctypes.c_uint64(0)
+    lens = (ctypes.c_int32 * 2)(1, 1)
+    assert lib.kvc_prefix_bytes(None, lens, ctypes.byref(n)) == kvc.KVC_ERR_INVALID_ARG
+    assert lib.kvc_save_prefix(None, lens, z, 4096, None) == kvc.KVC_ERR_INVALID_ARG
+    assert lib.kvc_load_prefix(None, z, 4096, lens, lens, None) == kvc.KVC_ERR_INVALID_ARG
