@@ -38,9 +38,16 @@
  *    host without a sync, so the kernels skip the offending sequence (append
  *    writes nothing for it, attention writes zeros for it) and raise a sticky
  *    per-cache flag that kvc_check() reports as KVC_ERR_DEVICE_RANGE.
- *  - No call allocates or synchronises except kvc_alloc, kvc_free and
- *    kvc_check (and every call when the environment variable KVC_SYNC_CHECK=1
- *    is set, which makes each launch synchronous and checked).
+ *  - No call allocates or synchronises except kvc_alloc, kvc_free,
+ *    kvc_alloc_paged, kvc_check and the prefix save/load calls (and every
+ *    call when the environment variable KVC_SYNC_CHECK=1 is set, which makes
+ *    each launch synchronous and checked).
+ *  - Each cache owns a workspace that its attention calls share: split
+ *    partials, self-resetting arrival counters, and the split of the work
+ *    cached for the last lengths seen (reused while the lengths, grid and
+ *    append mode stay the same, as across the layers of one decode step).
+ *    Calls on one cache must therefore not run concurrently: enqueue them on
+ *    one stream, or order the streams.
  */
 #ifndef KVC_H
 #define KVC_H

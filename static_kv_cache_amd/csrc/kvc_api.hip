@@ -310,6 +310,9 @@ kvc_status alloc_impl(const kvc_desc* desc, void* external, uint64_t bytes, int3
   if (ok) ok = hipMalloc((void**)&c->ws_cnt, cnt_bytes) == hipSuccess;
   if (ok) ok = hipMemset(c->ws_cnt, 0, cnt_bytes) == hipSuccess;
   if (ok) ok = hipMalloc((void**)&c->ws_map, (uint64_t)desc->batch * 2 * sizeof(int32_t)) == hipSuccess;
+  const uint64_t plan_bytes = ((uint64_t)KVC_PLAN_HEAD + (uint64_t)c->max_workgroups * KVC_PLAN_INTS) * 4;
+  if (ok) ok = hipMalloc((void**)&c->ws_plan, plan_bytes) == hipSuccess;
+  if (ok) ok = hipMemset(c->ws_plan, 0, plan_bytes) == hipSuccess;  // no plan yet
   if (ok) ok = hipMalloc((void**)&c->err_flag, 256) == hipSuccess;
   if (ok) ok = hipMemset(c->err_flag, 0, 256) == hipSuccess;
   if (ok && desc->attn == KVC_ATTN_MLA) {
@@ -340,6 +343,7 @@ kvc_status kvc_free(kvc_cache* c) {
   if (c->ws_cnt) (void)hipFree(c->ws_cnt);
   if (c->err_flag) (void)hipFree(c->err_flag);
   if (c->ws_map) (void)hipFree(c->ws_map);
+  if (c->ws_plan) (void)hipFree(c->ws_plan);
   if (c->ws_qabs) (void)hipFree(c->ws_qabs);
   if (c->ws_olat) (void)hipFree(c->ws_olat);
   delete c;

@@ -151,6 +151,7 @@ struct DecodeArgs {
   // from the cache, and written into the cache by the piece that ends there.
   const void* k_new;
   const void* v_new;
+  int32_t* plan;               // decode plan cache (KVC_PLAN_HEAD + n_wg * KVC_PLAN_INTS ints)
   // Block-table caches (null otherwise): k and v are the layer's pools
   // [num_blocks][H_kv][block_size][D] of pool_bytes bytes each, and row r of
   // sequence b lives in block table[b * table_width + (r >> block_shift)].
@@ -212,23 +213,21 @@ constexpr int kShareRest = KVC_SHARE_REST;
 //   m* = max_p m_p, l* = sum_p l_p 2^(m_p - m*), out = sum_p acc_p 2^(m_p - m*) / l*,
 // writes the chunk's output rows and resets the counter.
 struct SplitPiece {
-  long long s, seg_start;
+  long long s;
   int n, b, h0;
+  int w0, np;  // the segment's first workgroup and number of pieces
 };
 
 template <typename T, int D, int SH>
-__device__ void finish_splits(const DecodeArgs& a, const SplitPiece* sp, int nsp, int* s_flag,
-                              const Partition& part) {
+__device__ void finish_splits(const DecodeArgs& a, const SplitPiece* sp, int nsp, int* s_flag) {
   wait_stores();
   __syncthreads();
   if (threadIdx.x < nsp) {
     const SplitPiece& q = sp[threadIdx.x];
-    const int w0 = part.of(q.seg_start);
-    const int w1 = part.of(q.seg_start + q.n - 1);
     const int old = __hip_atomic_fetch_add(a.ws_cnt + q.s, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_flag[threadIdx.x * 3 + 0] = (old == w1 - w0) ? 1 : 0;
-    s_flag[threadIdx.x * 3 + 1] = w0;
-    s_flag[threadIdx.x * 3 + 2] = w1 - w0 + 1;
+    s_flag[threadIdx.x * 3 + 0] = (old == q.np - 1) ? 1 : 0;
+    s_flag[threadIdx.x * 3 + 1] = q.w0;
+    s_flag[threadIdx.x * 3 + 2] = q.np;
   }
   __syncthreads();
   // Merge in one round of loads: each thread requests (m_p, l_p, acc_p) of
@@ -1081,6 +1080,22 @@ struct I8Piece {
   }
 };
 
+// Decode plan cache. The split of the work (a workgroup's pieces) depends
+// only on the valid lengths, the grid and whether the launch appends, and
+// the layers of one decode step share all three. A launch that finds the
+// cached plan made for its lengths takes its pieces from its entry, loaded
+// together with the lengths, and starts streaming without the partition and
+// piece search. Otherwise it works the split out as usual, records its
+// entry, and the last workgroup to finish publishes the header (so no
+// workgroup of that launch can see a header whose entries are not written
+// yet). Launches with an empty or out-of-range sequence never publish.
+// Entry: piece count (-1: more than kPlanPieces), then per piece (b, hc,
+// r_begin, r_end, n, w0, np) with (w0, np) the segment's first workgroup
+// and number of pieces.
+constexpr int kPlanPieces = 8;
+constexpr int kPieceInts = 7;
+static_assert(1 + kPlanPieces * kPieceInts <= KVC_PLAN_INTS, "plan entry too small");
+
 // Persistent decode kernel: grid = W workgroups of 256 threads.
 template <class P>
 __global__ __launch_bounds__(kThreads)
@@ -1091,16 +1106,53 @@ void gqa_decode_kernel(DecodeArgs a) {
   __shared__ typename P::Smem sm;
   __shared__ int32_t s_prefix[KVC_MAX_BATCH + 1];
   __shared__ int32_t s_umax;  // longest segment in virtual rows
+  __shared__ int32_t s_entry[KVC_PLAN_INTS];
+  __shared__ int32_t s_same, s_key, s_last;
+  __shared__ int s_flag[6];
+  __shared__ SplitPiece split[2];  // a workgroup's first and last piece may be parts of segments
 
   const int B = a.batch;
   const int t = threadIdx.x;
-  build_row_space(a.valid_lens, a.cache_index, B, a.max_context, kSegRows, s_prefix, &s_umax, a.err_flag,
-                  blockIdx.x == 0, a.k_new ? 1 : 0);
-
-  const int HC = a.n_kv_heads * a.head_chunks;  // segments per sequence
-  const long long R = (long long)s_prefix[B] * HC;
   const int w = blockIdx.x;
+  const int min_rows = a.k_new ? 1 : 0;
+  int32_t* entry = a.plan + KVC_PLAN_HEAD + (size_t)w * KVC_PLAN_INTS;
+  // this workgroup's cached entry and the header, requested with the lengths
+  if (t >= 64 && t < 64 + KVC_PLAN_INTS) s_entry[t - 64] = entry[t - 64];
+  if (t == 128) s_key = a.plan[0] == 1 && a.plan[1] == a.n_wg && a.plan[2] == min_rows && a.plan[3] == B;
+  build_row_space(a.valid_lens, a.cache_index, B, a.max_context, kSegRows, s_prefix, &s_umax, a.err_flag,
+                  blockIdx.x == 0, min_rows, a.plan + KVC_PLAN_LENS, &s_same);
+  const bool fresh = !(s_key && s_same);  // no plan for these lengths: work it out and record it
+  const int HC = a.n_kv_heads * a.head_chunks;  // segments per sequence
+  int nsplit = 0;
 
+  if (!fresh && s_entry[0] >= 0) {
+    const int count = uniform(s_entry[0]);
+    for (int k = 0; k < count; ++k) {
+      const int32_t* pc = s_entry + 1 + k * kPieceInts;
+      const int b = uniform(pc[0]), hc = uniform(pc[1]), r_begin = uniform(pc[2]), r_end = uniform(pc[3]);
+      const int n = uniform(pc[4]);
+      const long long s = (long long)b * HC + hc;
+      const bool whole = r_begin == 0 && r_end == n;
+      const int kvg = hc / a.head_chunks;
+      const int chunk = hc % a.head_chunks;
+      P::run(a, sm, b, kvg, chunk, r_begin, r_end, n, whole, (long long)w + s);
+      if (!whole && nsplit < 2) {
+        if (threadIdx.x == 0) {  // read after the barriers in finish_splits
+          split[nsplit].s = s;
+          split[nsplit].n = n;
+          split[nsplit].b = b;
+          split[nsplit].h0 = kvg * (a.n_heads / a.n_kv_heads) + chunk * a.chunk_heads;
+          split[nsplit].w0 = pc[5];
+          split[nsplit].np = pc[6];
+        }
+        ++nsplit;
+      }
+    }
+    if (nsplit > 0) finish_splits<typename P::Elem, P::kD, P::kSlotHeads>(a, split, nsplit, s_flag);
+    return;
+  }
+
+  const long long R = (long long)s_prefix[B] * HC;
   // Empty (or out-of-range) sequences get zero outputs, spread over the grid.
   for (int bz = w; bz < B; bz += a.n_wg) {
     if (s_prefix[bz + 1] == s_prefix[bz]) {
@@ -1111,34 +1163,73 @@ void gqa_decode_kernel(DecodeArgs a) {
   }
 
   const Partition part(R, a.n_wg, s_umax, a.n_cus, a.wa, a.wb);
-  if (w >= part.W) return;
-  long long x = part.lo(w);
-  const long long hi = part.lo(w + 1);
-  if (x >= hi) return;
-  __shared__ int s_flag[6];
-  __shared__ SplitPiece split[2];  // a workgroup's first and last piece may be parts of segments
-  int nsplit = 0;
-
-  for_each_piece(s_prefix, B, HC, kSegRows, x, hi,
-                 [&](int b, int hc, int r_begin, int r_end, int n, long long real0) {
-    const long long s = (long long)b * HC + hc;
-    const bool whole = r_begin == 0 && r_end == n;
-    const int kvg = hc / a.head_chunks;
-    const int chunk = hc % a.head_chunks;
-    P::run(a, sm, b, kvg, chunk, r_begin, r_end, n, whole, (long long)w + s);
-    if (!whole && nsplit < 2) {
-      if (threadIdx.x == 0) {  // read after the barriers in finish_splits
-        split[nsplit].s = s;
-        split[nsplit].seg_start = real0;
-        split[nsplit].n = n;
-        split[nsplit].b = b;
-        split[nsplit].h0 = kvg * (a.n_heads / a.n_kv_heads) + chunk * a.chunk_heads;
+  int recorded = 0;  // pieces in this workgroup's new entry (thread 0), -1 past kPlanPieces
+  if (w < part.W) {
+    const long long x = part.lo(w);
+    const long long hi = part.lo(w + 1);
+    for_each_piece(s_prefix, B, HC, kSegRows, x, hi,
+                   [&](int b, int hc, int r_begin, int r_end, int n, long long real0) {
+      const long long s = (long long)b * HC + hc;
+      const bool whole = r_begin == 0 && r_end == n;
+      const int kvg = hc / a.head_chunks;
+      const int chunk = hc % a.head_chunks;
+      P::run(a, sm, b, kvg, chunk, r_begin, r_end, n, whole, (long long)w + s);
+      const int w0 = whole ? w : part.of(real0);
+      const int np = whole ? 1 : part.of(real0 + n - 1) - w0 + 1;
+      if (!whole && nsplit < 2) {
+        if (threadIdx.x == 0) {  // read after the barriers in finish_splits
+          split[nsplit].s = s;
+          split[nsplit].n = n;
+          split[nsplit].b = b;
+          split[nsplit].h0 = kvg * (a.n_heads / a.n_kv_heads) + chunk * a.chunk_heads;
+          split[nsplit].w0 = w0;
+          split[nsplit].np = np;
+        }
+        ++nsplit;
       }
-      ++nsplit;
+      if (fresh && threadIdx.x == 0 && recorded >= 0) {
+        if (recorded == kPlanPieces) {
+          recorded = -1;
+        } else {
+          int32_t* pc = entry + 1 + recorded * kPieceInts;
+          pc[0] = b;
+          pc[1] = hc;
+          pc[2] = r_begin;
+          pc[3] = r_end;
+          pc[4] = n;
+          pc[5] = w0;
+          pc[6] = np;
+          ++recorded;
+        }
+      }
+    });
+    if (nsplit > 0) finish_splits<typename P::Elem, P::kD, P::kSlotHeads>(a, split, nsplit, s_flag);
+  }
+  if (fresh && threadIdx.x == 0) {
+    entry[0] = recorded;
+    // the last workgroup of the launch publishes the header for these lengths
+    const int arrived = __hip_atomic_fetch_add(a.plan + 4, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = arrived == a.n_wg - 1;
+  }
+  if (fresh) {
+    __syncthreads();
+    if (s_last) {
+      bool all = true;
+      for (int b = t; b < B; b += kThreads) {
+        const int u = s_prefix[b + 1] - s_prefix[b];
+        all = all && u > 0;
+        a.plan[KVC_PLAN_LENS + b] = u > 0 ? u - kSegRows : 0;
+      }
+      const int usable = __syncthreads_and(all ? 1 : 0);
+      if (t == 0) {
+        a.plan[1] = a.n_wg;
+        a.plan[2] = min_rows;
+        a.plan[3] = B;
+        a.plan[4] = 0;
+        a.plan[0] = usable ? 1 : 0;
+      }
     }
-  });
-  if (nsplit > 0)
-    finish_splits<typename P::Elem, P::kD, P::kSlotHeads>(a, split, nsplit, s_flag, part);
+  }
 }
 
 template <class P, typename T, int D>
@@ -1225,6 +1316,7 @@ hipError_t kvc_launch_gqa_decode(const kvc_cache* c, const void* k_layer, const 
   a.err_flag = c->err_flag;
   a.k_new = k_new;
   a.v_new = v_new;
+  a.plan = c->ws_plan;
   a.k_scale = k_scale;
   a.v_scale = v_scale;
   a.table = block_table;

@@ -130,14 +130,17 @@ struct Partition {
 // (64 sequences per pass, an inclusive shuffle scan within the wave and a
 // running offset between passes); ends with a barrier that publishes them.
 // Every thread of the workgroup must call it. Out-of-range lengths raise
-// *err_flag when flag_errors is set.
+// *err_flag when flag_errors is set. With `snap`, *s_same tells whether
+// every length is non-zero and equal to snap[b].
 __device__ __forceinline__ void build_row_space(const int32_t* valid_lens, const int32_t* cache_index, int B,
                                                 int max_context, int seg_rows, int32_t* s_prefix,
                                                 int32_t* s_umax, int32_t* err_flag, bool flag_errors,
-                                                int min_rows = 0) {
+                                                int min_rows = 0, const int32_t* snap = nullptr,
+                                                int32_t* s_same = nullptr) {
   const int t = threadIdx.x;
   if (t < 64) {
     int carry = 0, umax = 0;
+    bool same = snap != nullptr;  // every length equal to snap[b] and non-zero
     for (int b0 = 0; b0 < B; b0 += 64) {
       const int b = b0 + t;
       int n = 0;
@@ -145,6 +148,7 @@ __device__ __forceinline__ void build_row_space(const int32_t* valid_lens, const
         bool bad;
         n = seq_rows(valid_lens, cache_index, b, max_context, min_rows, &bad);
         if (bad && flag_errors) atomicOr(err_flag, 1);
+        if (snap) same = same && n > 0 && snap[b] == n;
       }
       int x = n > 0 ? n + seg_rows : 0;
       umax = max(umax, x);
@@ -158,9 +162,11 @@ __device__ __forceinline__ void build_row_space(const int32_t* valid_lens, const
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) umax = max(umax, __shfl_xor(umax, off));
+    if (snap) same = __builtin_amdgcn_ballot_w64(!same) == 0;
     if (t == 0) {
       s_prefix[0] = 0;
       *s_umax = umax;
+      if (s_same) *s_same = same ? 1 : 0;
     }
   }
   __syncthreads();

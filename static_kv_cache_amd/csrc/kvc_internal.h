@@ -28,6 +28,7 @@ struct kvc_cache {
   uint64_t scale_kv_bytes;     // int8: offset of the V scales from the K scales in a layer
   uint8_t* scales;        // int8: [L][2][B][H_kv][S] float32 scales (after the codes), else NULL
   int32_t* ws_map;        // [B][2]: rows and first image row of each sequence's run (prefix save/load)
+  int32_t* ws_plan;       // decode plan cache: KVC_PLAN_HEAD ints, then KVC_PLAN_INTS per workgroup
   bool paged;             // block-table cache: layer = [K|V][num_blocks][H_kv][block_size][d_h]
   int block_size, block_shift, num_blocks, table_width;  // table_width = max_context / block_size
 
@@ -54,6 +55,13 @@ hipError_t kvc_launch_copy_rows(const void* src_k, const void* src_v, uint8_t* d
                                 int batch, int n_kv_heads, int t, int row_bytes, int max_context,
                                 const int32_t* dev_start, int host_start, int32_t* err_flag,
                                 hipStream_t stream);
+
+// Decode plan cache (kvc_decode.hip): header [valid, grid, min rows, batch,
+// arrival count, 0, 0, 0], the KVC_MAX_BATCH lengths the plan was made for,
+// then one entry of KVC_PLAN_INTS ints per workgroup.
+#define KVC_PLAN_LENS 8
+#define KVC_PLAN_HEAD (KVC_PLAN_LENS + KVC_MAX_BATCH)
+#define KVC_PLAN_INTS 64
 
 // Largest block table slice one decode piece keeps in LDS (blocks per sequence).
 #define KVC_MAX_TABLE 4096
