@@ -1080,22 +1080,6 @@ struct I8Piece {
   }
 };
 
-// Decode plan cache. The split of the work (a workgroup's pieces) depends
-// only on the valid lengths, the grid and whether the launch appends, and
-// the layers of one decode step share all three. A launch that finds the
-// cached plan made for its lengths takes its pieces from its entry, loaded
-// together with the lengths, and starts streaming without the partition and
-// piece search. Otherwise it works the split out as usual, records its
-// entry, and the last workgroup to finish publishes the header (so no
-// workgroup of that launch can see a header whose entries are not written
-// yet). Launches with an empty or out-of-range sequence never publish.
-// Entry: piece count (-1: more than kPlanPieces), then per piece (b, hc,
-// r_begin, r_end, n, w0, np) with (w0, np) the segment's first workgroup
-// and number of pieces.
-constexpr int kPlanPieces = 8;
-constexpr int kPieceInts = 7;
-static_assert(1 + kPlanPieces * kPieceInts <= KVC_PLAN_INTS, "plan entry too small");
-
 // Persistent decode kernel: grid = W workgroups of 256 threads.
 template <class P>
 __global__ __launch_bounds__(kThreads)
@@ -1106,8 +1090,7 @@ void gqa_decode_kernel(DecodeArgs a) {
   __shared__ typename P::Smem sm;
   __shared__ int32_t s_prefix[KVC_MAX_BATCH + 1];
   __shared__ int32_t s_umax;  // longest segment in virtual rows
-  __shared__ int32_t s_entry[KVC_PLAN_INTS];
-  __shared__ int32_t s_same, s_key, s_last;
+  __shared__ PlanState st;    // the cached split of the work (kvc_device.h)
   __shared__ int s_flag[6];
   __shared__ SplitPiece split[2];  // a workgroup's first and last piece may be parts of segments
 
@@ -1115,20 +1098,17 @@ void gqa_decode_kernel(DecodeArgs a) {
   const int t = threadIdx.x;
   const int w = blockIdx.x;
   const int min_rows = a.k_new ? 1 : 0;
-  int32_t* entry = a.plan + KVC_PLAN_HEAD + (size_t)w * KVC_PLAN_INTS;
-  // this workgroup's cached entry and the header, requested with the lengths
-  if (t >= 64 && t < 64 + KVC_PLAN_INTS) s_entry[t - 64] = entry[t - 64];
-  if (t == 128) s_key = a.plan[0] == 1 && a.plan[1] == a.n_wg && a.plan[2] == min_rows && a.plan[3] == B;
+  plan_fetch(a.plan, st, a.n_wg, min_rows, B);
   build_row_space(a.valid_lens, a.cache_index, B, a.max_context, kSegRows, s_prefix, &s_umax, a.err_flag,
-                  blockIdx.x == 0, min_rows, a.plan + KVC_PLAN_LENS, &s_same);
-  const bool fresh = !(s_key && s_same);  // no plan for these lengths: work it out and record it
+                  blockIdx.x == 0, min_rows, a.plan + KVC_PLAN_LENS, &st.same);
+  const bool fresh = !(st.key && st.same);  // no plan for these lengths: work it out and record it
   const int HC = a.n_kv_heads * a.head_chunks;  // segments per sequence
   int nsplit = 0;
 
-  if (!fresh && s_entry[0] >= 0) {
-    const int count = uniform(s_entry[0]);
+  if (!fresh && st.entry[0] >= 0) {
+    const int count = uniform(st.entry[0]);
     for (int k = 0; k < count; ++k) {
-      const int32_t* pc = s_entry + 1 + k * kPieceInts;
+      const int32_t* pc = st.entry + 1 + k * kPieceInts;
       const int b = uniform(pc[0]), hc = uniform(pc[1]), r_begin = uniform(pc[2]), r_end = uniform(pc[3]);
       const int n = uniform(pc[4]);
       const long long s = (long long)b * HC + hc;
@@ -1163,7 +1143,7 @@ void gqa_decode_kernel(DecodeArgs a) {
   }
 
   const Partition part(R, a.n_wg, s_umax, a.n_cus, a.wa, a.wb);
-  int recorded = 0;  // pieces in this workgroup's new entry (thread 0), -1 past kPlanPieces
+  int recorded = 0;  // pieces in this workgroup's new entry (thread 0)
   if (w < part.W) {
     const long long x = part.lo(w);
     const long long hi = part.lo(w + 1);
@@ -1187,49 +1167,11 @@ void gqa_decode_kernel(DecodeArgs a) {
         }
         ++nsplit;
       }
-      if (fresh && threadIdx.x == 0 && recorded >= 0) {
-        if (recorded == kPlanPieces) {
-          recorded = -1;
-        } else {
-          int32_t* pc = entry + 1 + recorded * kPieceInts;
-          pc[0] = b;
-          pc[1] = hc;
-          pc[2] = r_begin;
-          pc[3] = r_end;
-          pc[4] = n;
-          pc[5] = w0;
-          pc[6] = np;
-          ++recorded;
-        }
-      }
+      if (fresh) plan_record(a.plan, recorded, b, hc, r_begin, r_end, n, w0, np);
     });
     if (nsplit > 0) finish_splits<typename P::Elem, P::kD, P::kSlotHeads>(a, split, nsplit, s_flag);
   }
-  if (fresh && threadIdx.x == 0) {
-    entry[0] = recorded;
-    // the last workgroup of the launch publishes the header for these lengths
-    const int arrived = __hip_atomic_fetch_add(a.plan + 4, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = arrived == a.n_wg - 1;
-  }
-  if (fresh) {
-    __syncthreads();
-    if (s_last) {
-      bool all = true;
-      for (int b = t; b < B; b += kThreads) {
-        const int u = s_prefix[b + 1] - s_prefix[b];
-        all = all && u > 0;
-        a.plan[KVC_PLAN_LENS + b] = u > 0 ? u - kSegRows : 0;
-      }
-      const int usable = __syncthreads_and(all ? 1 : 0);
-      if (t == 0) {
-        a.plan[1] = a.n_wg;
-        a.plan[2] = min_rows;
-        a.plan[3] = B;
-        a.plan[4] = 0;
-        a.plan[0] = usable ? 1 : 0;
-      }
-    }
-  }
+  if (fresh) plan_publish(a.plan, st, recorded, s_prefix, B, kSegRows, a.n_wg, min_rows);
 }
 
 template <class P, typename T, int D>

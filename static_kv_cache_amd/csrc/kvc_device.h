@@ -172,6 +172,89 @@ __device__ __forceinline__ void build_row_space(const int32_t* valid_lens, const
   __syncthreads();
 }
 
+// ---- the cached split of the work ------------------------------------------
+//
+// The split (each workgroup's pieces) depends only on the valid lengths, the
+// grid and the append mode, which the layers of one decode step share. A
+// launch that finds the cached plan made for its lengths takes its pieces
+// from its entry, loaded together with the lengths, and starts streaming
+// without the partition and piece search. Otherwise it works the split out,
+// records its entry, and the last workgroup to finish publishes the header
+// (so no workgroup of that launch can see a header whose entries are not
+// written yet). Launches with an empty or out-of-range sequence never
+// publish. Layout (KVC_PLAN_* in kvc_internal.h): header [valid, grid, min
+// rows, batch, arrival count, 0, 0, 0], the lengths, then per workgroup a
+// piece count (-1: more than kPlanPieces) and kPieceInts ints per piece
+// (b, hc, r_begin, r_end, n, w0, np; w0, np = the segment's first workgroup
+// and number of pieces, for pieces that are part of a segment).
+constexpr int kPlanPieces = 8;
+constexpr int kPieceInts = 7;
+static_assert(1 + kPlanPieces * kPieceInts <= KVC_PLAN_INTS, "plan entry too small");
+
+struct PlanState {
+  int32_t entry[KVC_PLAN_INTS];  // this workgroup's cached entry
+  int32_t same, key, last;
+};
+
+// Requests this workgroup's entry and checks the header; every thread calls
+// it before build_row_space (whose barrier publishes the results), which
+// must be given snap = plan + KVC_PLAN_LENS and s_same = &st.same.
+__device__ __forceinline__ void plan_fetch(const int32_t* plan, PlanState& st, int n_wg, int min_rows, int B) {
+  const int t = threadIdx.x;
+  const int32_t* entry = plan + KVC_PLAN_HEAD + (size_t)blockIdx.x * KVC_PLAN_INTS;
+  if (t >= 64 && t < 64 + KVC_PLAN_INTS) st.entry[t - 64] = entry[t - 64];
+  if (t == 128) st.key = plan[0] == 1 && plan[1] == n_wg && plan[2] == min_rows && plan[3] == B;
+}
+
+// Records piece k of this workgroup's new entry (thread 0; `recorded` is its count, -1 once full).
+__device__ __forceinline__ void plan_record(int32_t* plan, int& recorded, int b, int hc, int r_begin, int r_end,
+                                            int n, int w0, int np) {
+  if (threadIdx.x != 0 || recorded < 0) return;
+  if (recorded == kPlanPieces) {
+    recorded = -1;
+    return;
+  }
+  int32_t* pc = plan + KVC_PLAN_HEAD + (size_t)blockIdx.x * KVC_PLAN_INTS + 1 + recorded * kPieceInts;
+  pc[0] = b;
+  pc[1] = hc;
+  pc[2] = r_begin;
+  pc[3] = r_end;
+  pc[4] = n;
+  pc[5] = w0;
+  pc[6] = np;
+  ++recorded;
+}
+
+// End of a launch that worked the split out: every thread calls it. Writes
+// the entry's count, counts the workgroup in, and the last workgroup of the
+// launch publishes the header for the lengths in s_prefix (u_b = n_b +
+// seg_rows per non-empty sequence).
+__device__ __forceinline__ void plan_publish(int32_t* plan, PlanState& st, int recorded, const int32_t* s_prefix,
+                                             int B, int seg_rows, int n_wg, int min_rows) {
+  const int t = threadIdx.x;
+  if (t == 0) {
+    plan[KVC_PLAN_HEAD + (size_t)blockIdx.x * KVC_PLAN_INTS] = recorded;
+    const int arrived = __hip_atomic_fetch_add(plan + 4, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    st.last = arrived == n_wg - 1;
+  }
+  __syncthreads();
+  if (!st.last) return;
+  bool all = true;
+  for (int b = t; b < B; b += blockDim.x) {
+    const int u = s_prefix[b + 1] - s_prefix[b];
+    all = all && u > 0;
+    plan[KVC_PLAN_LENS + b] = u > 0 ? u - seg_rows : 0;
+  }
+  const int usable = __syncthreads_and(all ? 1 : 0);
+  if (t == 0) {
+    plan[1] = n_wg;
+    plan[2] = min_rows;
+    plan[3] = B;
+    plan[4] = 0;
+    plan[0] = usable ? 1 : 0;
+  }
+}
+
 // Calls f(b, hc, r_begin, r_end, n, real0) for every piece of the row range
 // [x, hi): rows [r_begin, r_end) (r_end > r_begin) of segment (b, hc), whose
 // n real rows start at row-space position real0.
