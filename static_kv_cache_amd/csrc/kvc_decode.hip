@@ -320,8 +320,9 @@ struct ValuPiece {
 
   // Rows [r_begin, r_end) of segment (b, g, chunk). Writes the normalised
   // output when the piece is the whole segment, else the partial of `slot`.
-  static __device__ __forceinline__ void run(const DecodeArgs& a, Smem& sm, int b, int g, int chunk, int r_begin,
-                             int r_end, int n, bool whole, long long slot) {
+  static constexpr bool kSpeculative = true;  // nothing but shared memory is touched before the gate
+  static __device__ __forceinline__ bool run(const DecodeArgs& a, Smem& sm, int b, int g, int chunk, int r_begin,
+                             int r_end, int n, bool whole, long long slot, const int32_t* gate = nullptr) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int rs = lane / LPR;          // row slot of this lane
@@ -439,6 +440,10 @@ struct ValuPiece {
     int base = r_begin + wave * TILE;
     uint4 ka[U], va[U], kb[U], vb[U];
     load_tile(base, ka, va);
+    if (gate) {  // the piece was started before its inputs were confirmed
+      __syncthreads();
+      if (!*gate) return false;
+    }
     for (; base < r_end; base += 2 * stride) {
       load_tile(base + stride, kb, vb);
       use_any(base, ka, va);
@@ -508,6 +513,7 @@ struct ValuPiece {
       }
     }
     __syncthreads();  // the shared buffers are reused by the next piece
+    return true;
   }
 };
 
@@ -563,8 +569,12 @@ struct MfmaPiece {
     } u;
   };
 
-  static __device__ __forceinline__ void run(const DecodeArgs& a, Smem& sm, int b, int kvg, int chunk,
-                                             int r_begin, int r_end, int n, bool whole, long long slot) {
+  // The paged piece raises the device flag for table entries it reads
+  // before its first loads, so it is never started ahead of its inputs.
+  static constexpr bool kSpeculative = !PAGED;
+  static __device__ __forceinline__ bool run(const DecodeArgs& a, Smem& sm, int b, int kvg, int chunk,
+                                             int r_begin, int r_end, int n, bool whole, long long slot,
+                                             const int32_t* gate = nullptr) {
     b = uniform(b);
     kvg = uniform(kvg);
     chunk = uniform(chunk);
@@ -743,6 +753,10 @@ struct MfmaPiece {
         qb[k] = __builtin_bit_cast(bf16x8_t, v);
       }
     }
+    if (gate) {  // the piece was started before its inputs were confirmed
+      __syncthreads();
+      if (!*gate) return false;
+    }
     for (; base < r_end; base += NBUF * stride) {
 #pragma unroll
       for (int i = 0; i < NBUF; ++i) {
@@ -753,6 +767,7 @@ struct MfmaPiece {
 
     if constexpr (!PAGED) fused_write<uint16_t, D>(a, b, kvg, chunk, fresh);
     combine(a, sm, o, m, l, b, h0, whole, slot);
+    return true;
   }
 
   // End of a piece: combine the waves' (o, m, l) and write the output (whole
@@ -869,8 +884,10 @@ struct I8Piece {
     f32x4_t sk, sv;  // scales of rows 4g .. 4g + 3 of the tile
   };
 
-  static __device__ __forceinline__ void run(const DecodeArgs& a, Smem& sm, int b, int kvg, int chunk,
-                                             int r_begin, int r_end, int n, bool whole, long long slot) {
+  static constexpr bool kSpeculative = true;  // nothing but shared memory is touched before the gate
+  static __device__ __forceinline__ bool run(const DecodeArgs& a, Smem& sm, int b, int kvg, int chunk,
+                                             int r_begin, int r_end, int n, bool whole, long long slot,
+                                             const int32_t* gate = nullptr) {
     b = uniform(b);
     kvg = uniform(kvg);
     chunk = uniform(chunk);
@@ -1019,6 +1036,10 @@ struct I8Piece {
         qb[k] = __builtin_bit_cast(bf16x8_t, v);
       }
     }
+    if (gate) {  // the piece was started before its inputs were confirmed
+      __syncthreads();
+      if (!*gate) return false;
+    }
     // the loop is instantiated twice so that only the piece holding the new
     // row pays for the check
     auto stream = [&](auto patch_tag) {
@@ -1034,6 +1055,7 @@ struct I8Piece {
     else stream(std::integral_constant<bool, false>());
     if (fresh >= 0 && chunk == 0) write_new_row(a, sm, b, kvg, fresh);
     Base::combine(a, sm, o, m, l, b, h0, whole, slot);
+    return true;
   }
 
   // One wave quantises the new row of (b, g) from k_new (kv = 0) or v_new
@@ -1098,24 +1120,37 @@ void gqa_decode_kernel(DecodeArgs a) {
   const int t = threadIdx.x;
   const int w = blockIdx.x;
   const int min_rows = a.k_new ? 1 : 0;
-  plan_fetch(a.plan, st, a.n_wg, min_rows, B);
-  build_row_space(a.valid_lens, a.cache_index, B, a.max_context, kSegRows, s_prefix, &s_umax, a.err_flag,
-                  blockIdx.x == 0, min_rows, a.plan + KVC_PLAN_LENS, &st.same);
-  const bool fresh = !(st.key && st.same);  // no plan for these lengths: work it out and record it
   const int HC = a.n_kv_heads * a.head_chunks;  // segments per sequence
+  const int32_t* entry = plan_entry(a.plan);
+  const bool key = plan_key(a.plan, a.n_wg, min_rows, B);
+  const int count = uniform(key ? entry[0] : -1);  // pieces in this workgroup's cached entry
+  if (t < 64) {
+    scan_lengths(a.valid_lens, a.cache_index, B, a.max_context, kSegRows, s_prefix, &s_umax, a.err_flag,
+                 blockIdx.x == 0, min_rows, a.plan + KVC_PLAN_LENS, &st.gate);
+    if (t == 0) st.gate = st.gate && key;
+  }
+  // With a cached entry the first piece starts at once, before the lengths
+  // are confirmed: its loads stay inside the cache whatever they are, and it
+  // touches nothing but shared memory before its gate (a barrier after its
+  // first loads) confirms them. Otherwise the barrier comes first.
+  const bool speculate = P::kSpeculative && count >= 1;
+  if (!speculate) __syncthreads();  // publishes the prefix sums and the gate
   int nsplit = 0;
-
-  if (!fresh && st.entry[0] >= 0) {
-    const int count = uniform(st.entry[0]);
+  if (speculate || (st.gate && count >= 1)) {
+    bool planned = true;
     for (int k = 0; k < count; ++k) {
-      const int32_t* pc = st.entry + 1 + k * kPieceInts;
+      const int32_t* pc = entry + 1 + k * kPieceInts;
       const int b = uniform(pc[0]), hc = uniform(pc[1]), r_begin = uniform(pc[2]), r_end = uniform(pc[3]);
       const int n = uniform(pc[4]);
       const long long s = (long long)b * HC + hc;
       const bool whole = r_begin == 0 && r_end == n;
       const int kvg = hc / a.head_chunks;
       const int chunk = hc % a.head_chunks;
-      P::run(a, sm, b, kvg, chunk, r_begin, r_end, n, whole, (long long)w + s);
+      if (!P::run(a, sm, b, kvg, chunk, r_begin, r_end, n, whole, (long long)w + s,
+                  (k == 0 && speculate) ? &st.gate : nullptr)) {
+        planned = false;  // not this launch's plan: the gate's barrier published the prefix sums
+        break;
+      }
       if (!whole && nsplit < 2) {
         if (threadIdx.x == 0) {  // read after the barriers in finish_splits
           split[nsplit].s = s;
@@ -1128,9 +1163,13 @@ void gqa_decode_kernel(DecodeArgs a) {
         ++nsplit;
       }
     }
-    if (nsplit > 0) finish_splits<typename P::Elem, P::kD, P::kSlotHeads>(a, split, nsplit, s_flag);
-    return;
+    if (planned) {
+      if (nsplit > 0) finish_splits<typename P::Elem, P::kD, P::kSlotHeads>(a, split, nsplit, s_flag);
+      return;
+    }
   }
+  const bool fresh = !st.gate;  // no plan for these lengths: work it out and record it
+  if (!fresh && count == 0) return;  // the plan gives this workgroup nothing
 
   const long long R = (long long)s_prefix[B] * HC;
   // Empty (or out-of-range) sequences get zero outputs, spread over the grid.

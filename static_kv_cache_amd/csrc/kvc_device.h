@@ -128,17 +128,16 @@ struct Partition {
 
 // Prefix sums s_prefix[0..B] of u_b and the largest u_b, by the first wave
 // (64 sequences per pass, an inclusive shuffle scan within the wave and a
-// running offset between passes); ends with a barrier that publishes them.
-// Every thread of the workgroup must call it. Out-of-range lengths raise
+// running offset between passes), written to shared memory without a
+// barrier; only the first wave calls it. Out-of-range lengths raise
 // *err_flag when flag_errors is set. With `snap`, *s_same tells whether
 // every length is non-zero and equal to snap[b].
-__device__ __forceinline__ void build_row_space(const int32_t* valid_lens, const int32_t* cache_index, int B,
-                                                int max_context, int seg_rows, int32_t* s_prefix,
-                                                int32_t* s_umax, int32_t* err_flag, bool flag_errors,
-                                                int min_rows = 0, const int32_t* snap = nullptr,
-                                                int32_t* s_same = nullptr) {
+__device__ __forceinline__ void scan_lengths(const int32_t* valid_lens, const int32_t* cache_index, int B,
+                                             int max_context, int seg_rows, int32_t* s_prefix, int32_t* s_umax,
+                                             int32_t* err_flag, bool flag_errors, int min_rows,
+                                             const int32_t* snap, int32_t* s_same) {
   const int t = threadIdx.x;
-  if (t < 64) {
+  {
     int carry = 0, umax = 0;
     bool same = snap != nullptr;  // every length equal to snap[b] and non-zero
     for (int b0 = 0; b0 < B; b0 += 64) {
@@ -169,6 +168,17 @@ __device__ __forceinline__ void build_row_space(const int32_t* valid_lens, const
       if (s_same) *s_same = same ? 1 : 0;
     }
   }
+}
+
+// scan_lengths by the first wave, then a barrier that publishes the sums.
+// Every thread of the workgroup must call it.
+__device__ __forceinline__ void build_row_space(const int32_t* valid_lens, const int32_t* cache_index, int B,
+                                                int max_context, int seg_rows, int32_t* s_prefix,
+                                                int32_t* s_umax, int32_t* err_flag, bool flag_errors,
+                                                int min_rows = 0) {
+  if (threadIdx.x < 64)
+    scan_lengths(valid_lens, cache_index, B, max_context, seg_rows, s_prefix, s_umax, err_flag, flag_errors,
+                 min_rows, nullptr, nullptr);
   __syncthreads();
 }
 
@@ -177,8 +187,10 @@ __device__ __forceinline__ void build_row_space(const int32_t* valid_lens, const
 // The split (each workgroup's pieces) depends only on the valid lengths, the
 // grid and the append mode, which the layers of one decode step share. A
 // launch that finds the cached plan made for its lengths takes its pieces
-// from its entry, loaded together with the lengths, and starts streaming
-// without the partition and piece search. Otherwise it works the split out,
+// from its entry and starts streaming without the partition and piece
+// search (the decode kernel even starts its first piece before the lengths
+// have arrived, and confirms them at a barrier after the piece's first
+// loads). Otherwise it works the split out,
 // records its entry, and the last workgroup to finish publishes the header
 // (so no workgroup of that launch can see a header whose entries are not
 // written yet). Launches with an empty or out-of-range sequence never
@@ -192,18 +204,19 @@ constexpr int kPieceInts = 7;
 static_assert(1 + kPlanPieces * kPieceInts <= KVC_PLAN_INTS, "plan entry too small");
 
 struct PlanState {
-  int32_t entry[KVC_PLAN_INTS];  // this workgroup's cached entry
-  int32_t same, key, last;
+  int32_t gate;  // the header and the lengths match: the cached plan is for this launch
+  int32_t last;  // this workgroup publishes the new header
 };
 
-// Requests this workgroup's entry and checks the header; every thread calls
-// it before build_row_space (whose barrier publishes the results), which
-// must be given snap = plan + KVC_PLAN_LENS and s_same = &st.same.
-__device__ __forceinline__ void plan_fetch(const int32_t* plan, PlanState& st, int n_wg, int min_rows, int B) {
-  const int t = threadIdx.x;
-  const int32_t* entry = plan + KVC_PLAN_HEAD + (size_t)blockIdx.x * KVC_PLAN_INTS;
-  if (t >= 64 && t < 64 + KVC_PLAN_INTS) st.entry[t - 64] = entry[t - 64];
-  if (t == 128) st.key = plan[0] == 1 && plan[1] == n_wg && plan[2] == min_rows && plan[3] == B;
+// Whether the header names this launch's grid, append mode and batch (the
+// lengths are compared by scan_lengths). Uniform: every wave reads it.
+__device__ __forceinline__ bool plan_key(const int32_t* plan, int n_wg, int min_rows, int B) {
+  return plan[0] == 1 && plan[1] == n_wg && plan[2] == min_rows && plan[3] == B;
+}
+
+// This workgroup's cached entry.
+__device__ __forceinline__ const int32_t* plan_entry(const int32_t* plan) {
+  return plan + KVC_PLAN_HEAD + (size_t)blockIdx.x * KVC_PLAN_INTS;
 }
 
 // Records piece k of this workgroup's new entry (thread 0; `recorded` is its count, -1 once full).
