@@ -43,7 +43,8 @@ sys.path.insert(0, ROOT)
 METRIC = "decode-attention KV GB/s and % HBM peak; decode steps/s per layer at 1 GPU"
 HBM_PEAK_GBS = 8000.0
 WORKLOAD = "llama3_8b_gqa_bf16"
-KERNEL_SRC = os.path.join(ROOT, "static_kv_cache_amd", "csrc", "kvc_decode.hip")
+# the decode kernel's sources: the counter summary is used only if taken on these
+KERNEL_SRCS = [os.path.join(ROOT, "static_kv_cache_amd", "csrc", f) for f in ("kvc_decode.hip", "kvc_device.h")]
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "gqa_decode_llama3_8b_pmc.txt")
 
 
@@ -72,7 +73,10 @@ def parse():
 
 
 def kernel_sha():
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def read_pmc_traffic():
