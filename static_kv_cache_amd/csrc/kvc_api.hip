@@ -319,6 +319,8 @@ kvc_status alloc_impl(const kvc_desc* desc, void* external, uint64_t bytes, int3
     const uint64_t bh = (uint64_t)desc->batch * desc->n_heads;
     ok = hipMalloc((void**)&c->ws_qabs, bh * c->row_elems * sizeof(uint16_t)) == hipSuccess;
     if (ok) ok = hipMalloc((void**)&c->ws_olat, bh * desc->latent_dim * sizeof(uint16_t)) == hipSuccess;
+    const uint64_t chunks = ((uint64_t)desc->n_heads + 15) / 16;
+    if (ok) ok = hipMalloc((void**)&c->ws_seg, (uint64_t)desc->batch * chunks * 2 * sizeof(int32_t)) == hipSuccess;
   }
   if (ok) ok = hipDeviceSynchronize() == hipSuccess;
   if (!ok) {
@@ -344,6 +346,7 @@ kvc_status kvc_free(kvc_cache* c) {
   if (c->err_flag) (void)hipFree(c->err_flag);
   if (c->ws_map) (void)hipFree(c->ws_map);
   if (c->ws_plan) (void)hipFree(c->ws_plan);
+  if (c->ws_seg) (void)hipFree(c->ws_seg);
   if (c->ws_qabs) (void)hipFree(c->ws_qabs);
   if (c->ws_olat) (void)hipFree(c->ws_olat);
   delete c;

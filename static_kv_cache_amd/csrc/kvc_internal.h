@@ -29,6 +29,7 @@ struct kvc_cache {
   uint8_t* scales;        // int8: [L][2][B][H_kv][S] float32 scales (after the codes), else NULL
   int32_t* ws_map;        // [B][2]: rows and first image row of each sequence's run (prefix save/load)
   int32_t* ws_plan;       // decode plan cache: KVC_PLAN_HEAD ints, then KVC_PLAN_INTS per workgroup
+  int32_t* ws_seg;        // latent cache: [B][head chunks][2] first workgroup and pieces of each segment
   bool paged;             // block-table cache: layer = [K|V][num_blocks][H_kv][block_size][d_h]
   int block_size, block_shift, num_blocks, table_width;  // table_width = max_context / block_size
 

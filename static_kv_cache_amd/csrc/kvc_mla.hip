@@ -89,6 +89,7 @@ struct MlaArgs {
   int n_wg;
   int n_cus, wa, wb;           // partition weights: first n_cus workgroups wa, the rest wb
   int32_t* err_flag;
+  int32_t* seg_info;           // [B * head_chunks][2]: first workgroup and pieces of each non-empty segment
 };
 
 // Rows [r_begin, r_end) of sequence b against heads [hc * gc, (hc + 1) * gc).
@@ -290,24 +291,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const long long hi = part.lo(w + 1);
   if (x >= hi) return;
   for_each_piece(s_prefix, B, HC, kSegRowsMla, x, hi,
-                 [&](int b, int hc, int r_begin, int r_end, int, long long) {
-                   mla_piece(a, tile, sred, b, hc, r_begin, r_end, (long long)w + (long long)b * HC + hc);
+                 [&](int b, int hc, int r_begin, int r_end, int n, long long real0) {
+                   const long long s = (long long)b * HC + hc;
+                   mla_piece(a, tile, sred, b, hc, r_begin, r_end, (long long)w + s);
+                   if (r_begin == 0 && threadIdx.x == 0) {  // the segment's first piece: tell the merge
+                     a.seg_info[2 * s] = w;
+                     a.seg_info[2 * s + 1] = part.of(real0 + n - 1) - w + 1;
+                   }
                  });
 }
 
 // Merge of the pieces of segment (b, hc) for latent columns [64 y, 64 y + 64):
-// grid (B * HC, 8), 256 threads = 16 heads x 16 threads of 4 columns.
-// The partition is recomputed exactly as the split kernel made it.
+// grid (B * HC, 8), 256 threads = 16 heads x 16 threads of 4 columns. The
+// segment's first workgroup and number of pieces come from the split kernel
+// (written by the workgroup that held the segment's first piece), requested
+// together with the sequence's length.
 constexpr int kMergeCols = 64;
 __global__ __launch_bounds__(kThreads) void mla_merge_kernel(MlaArgs a) {
-  __shared__ int32_t s_prefix[KVC_MAX_BATCH + 1];
-  __shared__ int32_t s_umax;
   __shared__ float s_m[kMaxMerge * kSlotHeads];  // m_p of (piece p, head), head-minor
   __shared__ float s_l[kMaxMerge * kSlotHeads];  // l_p
   __shared__ float s_w[kMaxMerge * kSlotHeads];  // weight of the normalised partial
-  const int B = a.batch;
-  build_row_space(a.valid_lens, a.cache_index, B, a.max_context, kSegRowsMla, s_prefix, &s_umax, a.err_flag,
-                  false);
   const int HC = a.head_chunks;
   const int gc = a.chunk_heads;
   const int seg = blockIdx.x;
@@ -316,17 +319,14 @@ __global__ __launch_bounds__(kThreads) void mla_merge_kernel(MlaArgs a) {
   const int h = threadIdx.x >> 4;
   const int col = kMergeCols * blockIdx.y + 4 * (threadIdx.x & 15);
   uint16_t* o = a.out + ((size_t)b * a.n_heads + hc * gc + h) * kDc + col;
-  const int u = s_prefix[b + 1] - s_prefix[b];
-  if (u == 0) {  // empty or out-of-range sequence: zeros
+  bool bad;
+  const int n = seq_rows(a.valid_lens, a.cache_index, b, a.max_context, 0, &bad);
+  const int w0 = uniform(a.seg_info[2 * seg]);
+  const int np = uniform(a.seg_info[2 * seg + 1]);
+  if (n == 0) {  // empty or out-of-range sequence: zeros (the split kernel wrote no pieces)
     if (h < gc) *reinterpret_cast<uint2*>(o) = make_uint2(0u, 0u);
     return;
   }
-  const long long R = (long long)s_prefix[B] * HC;
-  const Partition part(R, a.n_wg, s_umax, a.n_cus, a.wa, a.wb);
-  const int n = u - kSegRowsMla;
-  const long long real0 = (long long)s_prefix[b] * HC + (long long)hc * u + kSegRowsMla;
-  const int w0 = part.of(real0);
-  const int np = part.of(real0 + n - 1) - w0 + 1;
   const long long slot0 = (long long)w0 + seg;
   // This thread's partial columns for the first K pieces are requested
   // before the weights are worked out, so both loads overlap.
@@ -474,6 +474,7 @@ hipError_t kvc_launch_mla_attn(const kvc_cache* c, const void* rows_layer, const
   a.wa = kShareFirstMla;
   a.wb = kShareRestMla;
   a.err_flag = c->err_flag;
+  a.seg_info = c->ws_seg;
   mla_split_kernel<<<dim3(a.n_wg), dim3(kThreads), 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
