@@ -17,8 +17,9 @@
 //    on the matrix cores. Work space as for GQA (row space of segments =
 //    (sequence, chunk of up to 16 heads), persistent grid, pieces). A
 //    workgroup streams its rows in tiles of 32 rows (36 KB, one contiguous
-//    block) staged through a skewed LDS tile; the next two tiles are in
-//    flight in registers while the current one is used. The latent rows are read from
+//    block) staged through two skewed LDS tiles used in turn (one barrier per
+//    tile besides the score exchange); the next two tiles are in flight in
+//    registers while the current one is used. The latent rows are read from
 //    HBM once for all heads of the chunk.
 //  - The score tile S = R_tile q~^T is split over the 576 dims: each wave
 //    takes a quarter (144 dims: four v_mfma_f32_16x16x32_bf16 steps and one
@@ -93,8 +94,9 @@ struct MlaArgs {
 };
 
 // Rows [r_begin, r_end) of sequence b against heads [hc * gc, (hc + 1) * gc).
-// sred: 8 KB of LDS for the per-wave partial score tiles.
-__device__ __forceinline__ void mla_piece(const MlaArgs& a, unsigned char* tile, f32x4_t* sred, int b, int hc,
+// tiles: two staged tiles used in turn; sred: 8 KB of LDS for the per-wave
+// partial score tiles.
+__device__ __forceinline__ void mla_piece(const MlaArgs& a, unsigned char* tiles, f32x4_t* sred, int b, int hc,
                                           int r_begin, int r_end, long long slot) {
   b = uniform(b);
   hc = uniform(hc);
@@ -130,7 +132,7 @@ __device__ __forceinline__ void mla_piece(const MlaArgs& a, unsigned char* tile,
 #pragma unroll
     for (int i = 0; i < kVec; ++i) st[i] = __builtin_amdgcn_raw_buffer_load_b128(res, off + i * 16 * kThreads, 0, 0);
   };
-  auto stage = [&](const u32x4_t (&st)[kVec]) {
+  auto stage = [&](unsigned char* tile, const u32x4_t (&st)[kVec]) {
 #pragma unroll
     for (int i = 0; i < kVec; ++i) {
       const int f = (int)threadIdx.x + i * kThreads;
@@ -139,7 +141,7 @@ __device__ __forceinline__ void mla_piece(const MlaArgs& a, unsigned char* tile,
   };
   // One tile whose rows start at t0 (rows at or past r_end are masked; a
   // tile wholly past the end changes nothing).
-  auto use_tile = [&](int t0) {
+  auto use_tile = [&](const unsigned char* tile, int t0) {
     // this wave's partial scores over its 144 dims, two 16-row blocks:
     // four steps of 32 dims (lane (g, j): row j, dims 32k + 8g ..) and one of 16
     f32x4_t sp[2];
@@ -148,7 +150,7 @@ __device__ __forceinline__ void mla_piece(const MlaArgs& a, unsigned char* tile,
     s16x4_t at[2];
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
-      const unsigned char* arow = tile + (16 * tb + j) * kStride + 2 * kQDims * wave;
+      const unsigned char* arow = tile + (16 * tb + j) * kStride + 2 * kQDims * wave;  // tile: this tile's rows
 #pragma unroll
       for (int k = 0; k < kQS; ++k) av[tb][k] = *reinterpret_cast<const bf16x8_t*>(arow + 64 * k + 16 * g);
       at[tb] = *reinterpret_cast<const s16x4_t*>(arow + 64 * kQS + 8 * g);
@@ -238,17 +240,21 @@ __device__ __forceinline__ void mla_piece(const MlaArgs& a, unsigned char* tile,
     const s16x4_t vt = *reinterpret_cast<const s16x4_t*>(qh + 32 * kQS + 4 * g);
     qt = real ? vt : s16x4_t{0, 0, 0, 0};
   }
+  // Two LDS tiles in turn: a wave stages tile i into buffer i % 2 only after
+  // the barrier of tile i - 1, which every wave reaches after it is done
+  // with tile i - 2 (the buffer's previous tile) and with its score
+  // exchange, so one barrier per tile (plus the exchange's) suffices.
+  unsigned char* const tile0 = tiles;
+  unsigned char* const tile1 = tiles + kTok * kStride;
   for (int t0 = r_begin; t0 < r_end; t0 += 2 * kTok) {
-    __syncthreads();  // every wave is done with the previous tile
-    stage(st0);
+    stage(tile0, st0);
     load(st0, t0 + 2 * kTok);
     __syncthreads();  // the tile is visible
-    use_tile(t0);
-    __syncthreads();
-    stage(st1);
+    use_tile(tile0, t0);
+    stage(tile1, st1);
     load(st1, t0 + 3 * kTok);
     __syncthreads();
-    use_tile(t0 + kTok);
+    use_tile(tile1, t0 + kTok);
   }
 
   // denominators of the head columns, then the partial o~ / l, m and l
@@ -269,13 +275,13 @@ __device__ __forceinline__ void mla_piece(const MlaArgs& a, unsigned char* tile,
     a.ml[((size_t)slot * kSlotHeads + j) * 2] = m;
     a.ml[((size_t)slot * kSlotHeads + j) * 2 + 1] = l;
   }
-  __syncthreads();  // the tile is reused by the next piece
+  __syncthreads();  // the tiles are reused by the next piece
 }
 
 // Persistent latent attention: grid = W workgroups of 256 threads, one per
 // CU by default, so each wave may use a whole SIMD's register file.
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void mla_split_kernel(MlaArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char tile[kTok * kStride];
+  __shared__ __attribute__((aligned(16))) unsigned char tile[2 * kTok * kStride];
   __shared__ f32x4_t sred[kWaves * 2 * 64];
   __shared__ int32_t s_prefix[KVC_MAX_BATCH + 1];
   __shared__ int32_t s_umax;
