@@ -639,6 +639,30 @@ def main():
     decode_ms = burst(wl.decode)
     log(f"bench: decode-only kernel, back-to-back bursts of {L}: mean {decode_ms * 1e3:.2f} us per launch")
 
+    # --- a decode loop's pattern: the lengths change once per step --------
+    # In a real loop every sequence grows by one row per step, and the 32
+    # layers of a step share the lengths, so the first launch of a step splits
+    # the work afresh and the other 31 reuse that split. Alternating
+    # cache_index between c and c - 1 reproduces that; the same step with an
+    # unchanged copy of cache_index separates the copy's own cost.
+    ci_host = wl.host["cache_index"].astype(np.int32)
+    alts = [wl.ci.clone(), wl.kvc.to_device(ci_host - 1, dev)]
+    same = [wl.ci.clone(), wl.ci.clone()]
+    def loop_ms(src):
+        k = [0]
+        def one():
+            wl.ci.copy_(src[k[0] % 2])
+            k[0] += 1
+            wl.step()
+        for _ in range(max(2, args.warmup)):
+            one()
+        return time_steps(torch, one, args.steps)
+    ms_loop_same = loop_ms(same)
+    ms_loop = loop_ms(alts)
+    wl.ci.copy_(alts[0])
+    log(f"bench: eager, lengths changing every step: {ms_loop:.4f} ms/step "
+        f"(unchanged lengths with the same copy: {ms_loop_same:.4f})")
+
     # --- graph replay of the whole step ---------------------------------
     ms_graph = None
     if not args.eager_only:
@@ -696,6 +720,8 @@ def main():
         "decode_steps_per_s": round(1.0 / (ms * 1e-3), 2),
         "eager_ms_per_step": round(ms_eager, 5),
         "eager_ms_per_step_two_launches": round(ms_two, 5),
+        "eager_ms_per_step_lengths_changing": round(ms_loop, 5),
+        "eager_ms_per_step_lengths_fixed_same_copy": round(ms_loop_same, 5),
         "config": {"workload": WORKLOAD, "n_layers": L, "batch": wl.B, "n_heads": wl.H,
                    "n_kv_heads": wl.Hkv, "head_dim": wl.D, "max_context": wl.S,
                    "valid_len": "U[1024,4096] seed 2", "sum_valid_len": wl.sum_valid,
