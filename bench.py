@@ -65,6 +65,7 @@ def parse():
     p.add_argument("--no-prefill", action="store_true", help="skip the prefill leg")
     p.add_argument("--no-paged", action="store_true", help="skip the block-table cache leg")
     p.add_argument("--no-prefix", action="store_true", help="skip the prefix save/load leg")
+    p.add_argument("--no-longctx", action="store_true", help="skip the long-context leg")
     p.add_argument("--mla-workgroups", type=int, default=0,
                    help="force the latent leg's persistent grid size (0 = device default)")
     p.add_argument("--workgroups", type=int, default=0,
@@ -426,6 +427,70 @@ def bench_paged(torch, steps, warmup, bf16_decode_us):
     return res
 
 
+def bench_longctx(torch, steps, warmup):
+    """The long-context shape: one sequence of 32,768 valid rows, H=64, H_kv=8,
+    d_h=128, bf16, on a cache allocated for 80 layers (10 GiB). One layer
+    (134 MB of K and V) fits the 256 MB Infinity Cache, so the launches rotate
+    over 8 filled layers (1.07 GB) to read from HBM. Decode attention
+    (kvc_decode_attn) and the layer step (kvc_append_decode_attn), per layer,
+    from HIP events around bursts of back-to-back launches."""
+    from static_kv_cache_amd import kvc, synthetic
+    dev = torch.device("cuda:0")
+    cfg = synthetic.WORKLOADS["longctx_gqa_bf16"]
+    Lalloc, B, H, Hkv, D, S = (cfg["n_layers"], cfg["batch"], cfg["n_heads"], cfg["n_kv_heads"],
+                               cfg["head_dim"], cfg["max_context"])
+    L = 8
+    cache = kvc.Cache(kvc.gqa_desc(Lalloc, B, H, Hkv, D, S, "bf16"))
+    c = synthetic.gqa_layer(cfg, seed_offset=0)
+    k = kvc.to_device(c["k_fill"], dev)
+    v = kvc.to_device(c["v_fill"], dev)
+    for layer in range(L):
+        cache.prefill_fill(layer, k, v, 0)
+    del k, v, c["k_fill"], c["v_fill"]
+    rng = np.random.default_rng(cfg["seed"] + 7)
+    q = [kvc.to_device(synthetic.draw(rng, (B, H, D), "bf16"), dev) for _ in range(L)]
+    kn = [kvc.to_device(synthetic.draw(rng, (B, Hkv, 1, D), "bf16"), dev) for _ in range(L)]
+    vn = [kvc.to_device(synthetic.draw(rng, (B, Hkv, 1, D), "bf16"), dev) for _ in range(L)]
+    out = [torch.empty((B, H, D), dtype=torch.bfloat16, device=dev) for _ in range(L)]
+    valid = kvc.to_device(c["valid_lens"], dev)
+    ci = kvc.to_device(c["cache_index"], dev)
+    sm = c["sm_scale"]
+    sum_valid = int(c["valid_lens"].sum())
+    kv_bytes = sum_valid * 2 * Hkv * D * 2
+
+    def decode(layer):
+        cache.decode_attn(layer, q[layer], out[layer], valid_lens=valid, cache_index=ci, sm_scale=sm)
+
+    def step(layer):
+        cache.append_decode_attn(layer, kn[layer], vn[layer], q[layer], out[layer], ci, sm)
+
+    def burst(fn):
+        for _ in range(warmup):
+            for layer in range(L):
+                fn(layer)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        torch.cuda.synchronize()
+        for e0, e1 in evs:
+            e0.record()
+            for layer in range(L):
+                fn(layer)
+            e1.record()
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) / L for a, b in evs]))
+
+    dec_ms = burst(decode)
+    step_ms = burst(step)
+    cache.check()
+    cache.free()
+    gbs = kv_bytes / (dec_ms * 1e-3) / 1e9
+    log(f"bench: long context decode {dec_ms * 1e3:.2f} us ({gbs:.1f} GB/s), step {step_ms * 1e3:.2f} us")
+    return dict(workload="longctx_gqa_bf16", batch=B, n_heads=H, n_kv_heads=Hkv, head_dim=D, max_context=S,
+                valid_len=sum_valid, layers_allocated=Lalloc, layers_rotated=L, kv_bytes_per_layer=kv_bytes,
+                decode_us=round(dec_ms * 1e3, 3), kv_gbs=round(gbs, 2), hbm_peak_frac=round(gbs / HBM_PEAK_GBS, 4),
+                step_us=round(step_ms * 1e3, 3), layer_steps_per_s=round(1.0 / (step_ms * 1e-3), 1),
+                step="kvc_append_decode_attn (append + decode attention, one launch), per layer")
+
+
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
@@ -701,6 +766,7 @@ def main():
     mla = None if args.no_mla else bench_mla(torch, max(5, args.steps // 2), 2, args.mla_workgroups)
     i8 = None if args.no_i8 else bench_i8(torch, max(5, args.steps // 2), 2, decode_ms * 1e3)
     paged = None if args.no_paged else bench_paged(torch, max(5, args.steps // 2), 2, decode_ms * 1e3)
+    longctx = None if args.no_longctx else bench_longctx(torch, max(5, args.steps // 2), 2)
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl, args.cpu_repeats)
     line = {
         "metric": METRIC,
@@ -735,6 +801,7 @@ def main():
         "prefill": prefill,
         "paged": paged,
         "prefix": prefix,
+        "longctx": longctx,
     }
     print(json.dumps(line), flush=True)
 

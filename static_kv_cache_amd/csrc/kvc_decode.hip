@@ -218,6 +218,54 @@ struct SplitPiece {
   int w0, np;  // the segment's first workgroup and number of pieces
 };
 
+#ifndef KVC_MERGE_WIDE
+#define KVC_MERGE_WIDE 16  // pieces per round of loads when a segment has more than 8 (32 measured the same)
+#endif
+
+// 64-bit coherent load of a partial written by another workgroup (two floats)
+__device__ __forceinline__ void get2(const float* p, float& x, float& y) {
+  const uint64_t u = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  x = __uint_as_float((uint32_t)u);
+  y = __uint_as_float((uint32_t)(u >> 32));
+}
+
+// The merged output dims d .. d + 3 of head h of segment s, whose np pieces
+// sit in slots w0 + s .. w0 + s + np - 1, in batches of K pieces.
+template <int D, int SH, int K>
+__device__ __forceinline__ void merge_group(const DecodeArgs& a, long long s, int w0, int np, int h, int d,
+                                            float (&out)[4]) {
+  float mx = -INFINITY, ls = 0.0f;
+  float x[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int p0 = 0; p0 < np; p0 += K) {
+    float mm[K], ll[K], aa[K][4];
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      const size_t ent = ((size_t)(w0 + min(p0 + i, np - 1) + s)) * SH + h;
+      get2(a.ws_ml + ent * 2, mm[i], ll[i]);
+      get2(a.ws_acc + ent * D + d, aa[i][0], aa[i][1]);
+      get2(a.ws_acc + ent * D + d + 2, aa[i][2], aa[i][3]);
+    }
+    float bm = mx;
+#pragma unroll
+    for (int i = 0; i < K; ++i) bm = (p0 + i < np) ? fmaxf(bm, mm[i]) : bm;
+    const float c = __builtin_amdgcn_exp2f(mx - bm);  // 0 on the first batch (mx = -inf)
+    ls *= c;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] *= c;
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      const float f = (p0 + i < np) ? __builtin_amdgcn_exp2f(mm[i] - bm) : 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = fmaf(aa[i][e], f, x[e]);
+      ls = fmaf(ll[i], f, ls);
+    }
+    mx = bm;
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) out[e] = x[e] / ls;
+}
+
 template <typename T, int D, int SH>
 __device__ void finish_splits(const DecodeArgs& a, const SplitPiece* sp, int nsp, int* s_flag) {
   wait_stores();
@@ -230,66 +278,67 @@ __device__ void finish_splits(const DecodeArgs& a, const SplitPiece* sp, int nsp
     s_flag[threadIdx.x * 3 + 2] = q.np;
   }
   __syncthreads();
-  // Merge in one round of loads: each thread requests (m_p, l_p, acc_p) of
-  // its output elements for a batch of pieces at once and folds them into a
-  // running (maximum, denominator, sum), rescaling when a batch raises the
-  // maximum.
+  // Merge in one round of loads where the segment has at most 8 pieces (a
+  // decode batch): each thread requests (m_p, l_p, acc_p) of its output
+  // elements for all pieces at once and folds them into a running
+  // (maximum, denominator, sum). A longer segment (one sequence split over
+  // the grid) is merged four dims per thread, KW pieces per round of loads.
   const int gc = a.chunk_heads;
   constexpr int E = 2;  // output elements per thread and pass
   constexpr int K = 8;  // pieces per batch of loads
+  constexpr int DV = D / 4;  // four-dim groups per head (long segments)
   for (int k = 0; k < nsp; ++k) {
     if (!s_flag[k * 3]) continue;
     const SplitPiece& q = sp[k];
     const int w0 = s_flag[k * 3 + 1];
     const int np = s_flag[k * 3 + 2];
     T* o = reinterpret_cast<T*>(a.out) + ((size_t)q.b * a.n_heads + q.h0) * D;
-    for (int base = 0; base < gc * D; base += E * kThreads) {
-      int h[E], d[E];
+    if (np > K) {
+      for (int v0 = 0; v0 < gc * DV; v0 += kThreads) {
+        const int vi = min(v0 + (int)threadIdx.x, gc * DV - 1);
+        const int h = vi / DV;
+        const int d = 4 * (vi - h * DV);
+        float x[4];
+        merge_group<D, SH, KVC_MERGE_WIDE>(a, q.s, w0, np, h, d, x);
+        if (v0 + (int)threadIdx.x < gc * DV) {
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const int idx = min(base + e * kThreads + (int)threadIdx.x, gc * D - 1);
-        h[e] = idx / D;
-        d[e] = idx - h[e] * D;
+          for (int e = 0; e < 4; ++e) store_out(o + h * D + d + e, x[e]);
+        }
       }
-      float mx[E], ls[E], x[E];
+    } else {
+      for (int base = 0; base < gc * D; base += E * kThreads) {
+        int h[E], d[E];
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        mx[e] = -INFINITY;
-        ls[e] = 0.0f;
-        x[e] = 0.0f;
-      }
-      for (int p0 = 0; p0 < np; p0 += K) {
+        for (int e = 0; e < E; ++e) {
+          const int idx = min(base + e * kThreads + (int)threadIdx.x, gc * D - 1);
+          h[e] = idx / D;
+          d[e] = idx - h[e] * D;
+        }
         float mm[E][K], ll[E][K], aa[E][K];
 #pragma unroll
         for (int e = 0; e < E; ++e)
 #pragma unroll
           for (int i = 0; i < K; ++i) {
-            const size_t ent = ((size_t)(w0 + min(p0 + i, np - 1) + q.s)) * SH + h[e];
+            const size_t ent = ((size_t)(w0 + min(i, np - 1) + q.s)) * SH + h[e];
             mm[e][i] = get(a.ws_ml + ent * 2);
             ll[e][i] = get(a.ws_ml + ent * 2 + 1);
             aa[e][i] = get(a.ws_acc + ent * D + d[e]);
           }
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-          float bm = mx[e];
+          float bm = -INFINITY;
 #pragma unroll
-          for (int i = 0; i < K; ++i) bm = (p0 + i < np) ? fmaxf(bm, mm[e][i]) : bm;
-          const float c = __builtin_amdgcn_exp2f(mx[e] - bm);  // 0 on the first batch (mx = -inf)
-          x[e] *= c;
-          ls[e] *= c;
+          for (int i = 0; i < K; ++i) bm = (i < np) ? fmaxf(bm, mm[e][i]) : bm;
+          float x = 0.0f, ls = 0.0f;
 #pragma unroll
           for (int i = 0; i < K; ++i) {
-            const float f = (p0 + i < np) ? __builtin_amdgcn_exp2f(mm[e][i] - bm) : 0.0f;
-            x[e] = fmaf(aa[e][i], f, x[e]);
-            ls[e] = fmaf(ll[e][i], f, ls[e]);
+            const float f = (i < np) ? __builtin_amdgcn_exp2f(mm[e][i] - bm) : 0.0f;
+            x = fmaf(aa[e][i], f, x);
+            ls = fmaf(ll[e][i], f, ls);
           }
-          mx[e] = bm;
+          const int idx = base + e * kThreads + (int)threadIdx.x;
+          if (idx < gc * D) store_out(o + idx, x / ls);
         }
-      }
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const int idx = base + e * kThreads + (int)threadIdx.x;
-        if (idx < gc * D) store_out(o + idx, x[e] / ls[e]);
       }
     }
     if (threadIdx.x == 0) __hip_atomic_store(a.ws_cnt + q.s, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

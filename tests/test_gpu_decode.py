@@ -244,6 +244,27 @@ def test_fewer_rows_than_workgroups(workgroups):
     cache.free()
 
 
+@pytest.mark.parametrize("dtype,H,Hkv,D,S,workgroups", [
+    ("bf16", 8, 1, 128, 8192, 64),     # 8 pieces or so: the batch merge
+    ("bf16", 8, 1, 128, 8192, 256),    # ~32 pieces: two rounds of the wide merge
+    ("bf16", 16, 2, 64, 6000, 1024),   # ~500 pieces per segment
+    ("f32", 8, 2, 256, 4000, 512),     # the fp32 piece, 256-wide heads
+    ("bf16", 64, 8, 128, 12345, 300),  # eight heads per kv head, ragged rows
+])
+def test_one_long_sequence_wide_merge(dtype, H, Hkv, D, S, workgroups):
+    """One sequence split over the grid: each segment's pieces (more than 8
+    past 64 workgroups) are merged four dims per thread in rounds of loads."""
+    dev = device()
+    case = synthetic.random_gqa_case(81, 1, H, Hkv, D, S, dtype, valid_lens=[S])
+    cache = kvc.Cache(kvc.gqa_desc(1, 1, H, Hkv, D, S, dtype))
+    wg = min(workgroups, cache.workgroups()[1])
+    cache.free()
+    say(f"one long sequence: {dtype} H={H} H_kv={Hkv} D={D} S={S} workgroups={wg}")
+    cache, ref, out, want = run_case(dev, case, workgroups=wg, dtype=dtype)
+    tol_check(to_f64(out), want, dtype, "long sequence")
+    cache.free()
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_skewed_lengths_many_pieces(dtype):
     """One full-length sequence among many of one to three rows, with the
