@@ -68,6 +68,8 @@ def parse():
     p.add_argument("--no-longctx", action="store_true", help="skip the long-context leg")
     p.add_argument("--mla-workgroups", type=int, default=0,
                    help="force the latent leg's persistent grid size (0 = device default)")
+    p.add_argument("--longctx-workgroups", type=int, default=0,
+                   help="force the long-context leg's persistent grid size (0 = device default)")
     p.add_argument("--workgroups", type=int, default=0,
                    help="force the persistent attention grid size (0 = device default)")
     return p.parse_args()
@@ -427,7 +429,7 @@ def bench_paged(torch, steps, warmup, bf16_decode_us):
     return res
 
 
-def bench_longctx(torch, steps, warmup):
+def bench_longctx(torch, steps, warmup, workgroups=0):
     """The long-context shape: one sequence of 32,768 valid rows, H=64, H_kv=8,
     d_h=128, bf16, on a cache allocated for 80 layers (10 GiB). One layer
     (134 MB of K and V) fits the 256 MB Infinity Cache, so the launches rotate
@@ -441,6 +443,8 @@ def bench_longctx(torch, steps, warmup):
                                cfg["head_dim"], cfg["max_context"])
     L = 8
     cache = kvc.Cache(kvc.gqa_desc(Lalloc, B, H, Hkv, D, S, "bf16"))
+    if workgroups:
+        cache.set_workgroups(workgroups)
     c = synthetic.gqa_layer(cfg, seed_offset=0)
     k = kvc.to_device(c["k_fill"], dev)
     v = kvc.to_device(c["v_fill"], dev)
@@ -766,7 +770,7 @@ def main():
     mla = None if args.no_mla else bench_mla(torch, max(5, args.steps // 2), 2, args.mla_workgroups)
     i8 = None if args.no_i8 else bench_i8(torch, max(5, args.steps // 2), 2, decode_ms * 1e3)
     paged = None if args.no_paged else bench_paged(torch, max(5, args.steps // 2), 2, decode_ms * 1e3)
-    longctx = None if args.no_longctx else bench_longctx(torch, max(5, args.steps // 2), 2)
+    longctx = None if args.no_longctx else bench_longctx(torch, max(5, args.steps // 2), 2, args.longctx_workgroups)
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl, args.cpu_repeats)
     line = {
         "metric": METRIC,

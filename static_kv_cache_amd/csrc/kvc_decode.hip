@@ -222,14 +222,6 @@ struct SplitPiece {
 #define KVC_MERGE_WIDE 16  // pieces per round of loads when a segment has more than 8 (32 measured the same)
 #endif
 
-// 64-bit coherent load of a partial written by another workgroup (two floats)
-__device__ __forceinline__ void get2(const float* p, float& x, float& y) {
-  const uint64_t u = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-  x = __uint_as_float((uint32_t)u);
-  y = __uint_as_float((uint32_t)(u >> 32));
-}
-
 // The merged output dims d .. d + 3 of head h of segment s, whose np pieces
 // sit in slots w0 + s .. w0 + s + np - 1, in batches of K pieces.
 template <int D, int SH, int K>

@@ -71,6 +71,13 @@ __device__ __forceinline__ void put(float* p, float v) {
 __device__ __forceinline__ float get(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// the same for two consecutive floats (8-byte aligned), in one load
+__device__ __forceinline__ void get2(const float* p, float& x, float& y) {
+  const uint64_t u = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  x = __uint_as_float((uint32_t)u);
+  y = __uint_as_float((uint32_t)(u >> 32));
+}
 // s_waitcnt vmcnt(0) (expcnt, lgkmcnt left alone): this thread's stores are done
 __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
