@@ -68,6 +68,8 @@ def parse():
     p.add_argument("--no-longctx", action="store_true", help="skip the long-context leg")
     p.add_argument("--mla-workgroups", type=int, default=0,
                    help="force the latent leg's persistent grid size (0 = device default)")
+    p.add_argument("--i8-workgroups", type=int, default=0,
+                   help="force the int8 leg's persistent grid size (0 = device default)")
     p.add_argument("--longctx-workgroups", type=int, default=0,
                    help="force the long-context leg's persistent grid size (0 = device default)")
     p.add_argument("--workgroups", type=int, default=0,
@@ -303,12 +305,14 @@ class I8Workload:
         self.decode(layer)
 
 
-def bench_i8(torch, steps, warmup, bf16_decode_us):
+def bench_i8(torch, steps, warmup, bf16_decode_us, workgroups=0):
     """Decode attention on the int8 cache (kvc_decode_attn) and the layer step
     (kvc_append_decode_attn: quantise the new rows, append and attend in one
     launch; the two-launch form beside it), per layer, from HIP events around
     bursts of back-to-back launches over the 32 layers."""
     wl = I8Workload(torch, torch.device("cuda:0"))
+    if workgroups:
+        wl.cache.set_workgroups(workgroups)
     L = wl.L
 
     def burst(fn):
@@ -768,7 +772,7 @@ def main():
     prefix = None if args.no_prefix else bench_prefix(torch, wl, 5, prefill)
     wl.cache.free()
     mla = None if args.no_mla else bench_mla(torch, max(5, args.steps // 2), 2, args.mla_workgroups)
-    i8 = None if args.no_i8 else bench_i8(torch, max(5, args.steps // 2), 2, decode_ms * 1e3)
+    i8 = None if args.no_i8 else bench_i8(torch, max(5, args.steps // 2), 2, decode_ms * 1e3, args.i8_workgroups)
     paged = None if args.no_paged else bench_paged(torch, max(5, args.steps // 2), 2, decode_ms * 1e3)
     longctx = None if args.no_longctx else bench_longctx(torch, max(5, args.steps // 2), 2, args.longctx_workgroups)
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl, args.cpu_repeats)

@@ -362,6 +362,7 @@ struct ValuPiece {
   // Rows [r_begin, r_end) of segment (b, g, chunk). Writes the normalised
   // output when the piece is the whole segment, else the partial of `slot`.
   static constexpr bool kSpeculative = true;  // nothing but shared memory is touched before the gate
+  static constexpr int kWgPerCu = 1;
   static __device__ __forceinline__ bool run(const DecodeArgs& a, Smem& sm, int b, int g, int chunk, int r_begin,
                              int r_end, int n, bool whole, long long slot, const int32_t* gate = nullptr) {
     const int lane = threadIdx.x & 63;
@@ -613,6 +614,9 @@ struct MfmaPiece {
   // The paged piece raises the device flag for table entries it reads
   // before its first loads, so it is never started ahead of its inputs.
   static constexpr bool kSpeculative = !PAGED;
+  // One workgroup per CU: measured faster than the two a CU could hold (fewer
+  // pieces to merge, no second workgroup competing for issue slots and LDS).
+  static constexpr int kWgPerCu = 1;
   static __device__ __forceinline__ bool run(const DecodeArgs& a, Smem& sm, int b, int kvg, int chunk,
                                              int r_begin, int r_end, int n, bool whole, long long slot,
                                              const int32_t* gate = nullptr) {
@@ -912,7 +916,13 @@ struct I8Piece {
   static constexpr int KL = D / 64;           // K code vectors per lane per tile (D / 4 codes)
   static constexpr int VL = TR * CPR / 64;    // V code vectors per lane per tile
   static constexpr int VSTRIDE = Base::VSTRIDE;
-  static constexpr int NBUF = Base::NBUF;
+  static constexpr int NBUF = Base::NBUF;  // (three tiles measured the same, four slower)
+  // Two workgroups per CU where the registers allow (d_h <= 128): the int8
+  // tile's conversions make each wave's chain long enough that a second
+  // wave per SIMD pays, above all in the fused launch, whose piece with the
+  // new row quantises it behind a barrier (layer step 26.2 -> 24.4 us; the
+  // decode alone 25.0 -> 24.9 us).
+  static constexpr int kWgPerCu = D <= 128 ? 2 : 1;
   static_assert(D >= 64 && D % 64 == 0 && VL >= 1, "int8 head_dim must be 64, 128 or 256");
   struct Smem : Base::Smem {
     __attribute__((aligned(16))) int8_t nq[2][D];  // fused append: the new K and V rows' codes
@@ -1259,10 +1269,9 @@ hipError_t launch_piece(const kvc_cache* c, DecodeArgs a, int chunk_heads, hipSt
   const int group = c->d.n_heads / c->d.n_kv_heads;
   a.chunk_heads = chunk_heads;
   a.head_chunks = group / chunk_heads;
-  // One workgroup per CU by default: measured faster than filling every CU
-  // with the two workgroups it could hold (fewer pieces to merge, and no
-  // second workgroup competing for the CU's issue slots and LDS).
-  a.n_wg = c->workgroups_forced > 0 ? c->workgroups_forced : c->num_cus;
+  // P::kWgPerCu workgroups per CU by default (one for the bf16 and fp32
+  // pieces, two for the int8 piece where its registers allow; see there).
+  a.n_wg = c->workgroups_forced > 0 ? c->workgroups_forced : c->num_cus * P::kWgPerCu;
   if (a.n_wg > c->max_workgroups) a.n_wg = c->max_workgroups;
   a.n_cus = c->num_cus;
   a.wa = kShareFirst;
