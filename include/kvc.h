@@ -292,6 +292,25 @@ kvc_status kvc_paged_decode_attn(kvc_cache* cache, int32_t layer, const void* q,
                                  const int32_t* block_table, const int32_t* valid_lens,
                                  const int32_t* cache_index, float sm_scale, void* stream);
 
+/* One decode step of one layer of a paged cache in one launch: the same
+ * result as
+ *   kvc_paged_append(cache, layer, k_new, v_new, block_table, cache_index, 1, stream);
+ *   kvc_paged_decode_attn(cache, layer, q, out, block_table, NULL, cache_index, sm_scale, stream);
+ * ("10.3 ...", section 5 step 2, through the block table of section 7.2):
+ * the new row is written at cache_index[b] through the table and attended
+ * with rows [0, cache_index[b]), straight from k_new / v_new, so the output
+ * bits equal those of the two calls. A sequence with cache_index[b] outside
+ * [0, max_context) is skipped (no write, zero output) and raises the
+ * device-range flag; if the new row's table entry lies outside
+ * [0, num_blocks), nothing is written, that block's rows (the new one
+ * included) read as zeros and the flag is raised, as after the two calls.
+ * Unlike the two calls, a sequence that reads a block into which another
+ * sequence of the same call writes its new row may see that row before or
+ * after the write. Shapes as for kvc_append_decode_attn. */
+kvc_status kvc_paged_append_decode_attn(kvc_cache* cache, int32_t layer, const void* k_new, const void* v_new,
+                                        const void* q, void* out, const int32_t* block_table,
+                                        const int32_t* cache_index, float sm_scale, void* stream);
+
 /* ---- live-prefix save and load -------------------------------------------
  * "KV Cache Optimization: GQA Audit, In-Place Buffers, Persistent Prompts",
  * "#3 Persistent KV across sessions" and its file map: the cache after a

@@ -638,6 +638,21 @@ kvc_status kvc_paged_decode_attn(kvc_cache* c, int32_t layer, const void* q, voi
   return after_launch(c, e, s);
 }
 
+kvc_status kvc_paged_append_decode_attn(kvc_cache* c, int32_t layer, const void* k_new, const void* v_new,
+                                        const void* q, void* out, const int32_t* block_table,
+                                        const int32_t* cache_index, float sm_scale, void* stream) {
+  if (!c || !c->paged || !layer_ok(c, layer) || !k_new || !v_new || !q || !out || !block_table || !cache_index)
+    return KVC_ERR_INVALID_ARG;
+  if (!(sm_scale > 0.0f) || sm_scale > 3.0e38f) return KVC_ERR_INVALID_ARG;
+  void* kl;
+  void* vl;
+  kvc_layer_ptrs(c, layer, &kl, &vl);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = kvc_launch_gqa_decode(c, kl, vl, q, out, nullptr, cache_index, sm_scale, s, k_new, v_new,
+                                       nullptr, nullptr, block_table);
+  return after_launch(c, e, s);
+}
+
 kvc_status kvc_set_workgroups(kvc_cache* c, int32_t n) {
   if (!c || n < 0 || n > c->max_workgroups) return KVC_ERR_INVALID_ARG;
   c->workgroups_forced = n;

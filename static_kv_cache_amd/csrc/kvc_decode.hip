@@ -655,7 +655,7 @@ struct MfmaPiece {
     // and their scores are masked below.
     // Fused append: the new row `fresh` lies outside the resources (it reads
     // as zeros) and is taken from k_new / v_new by the lanes that hold it.
-    const int fresh = PAGED ? -1 : uniform(fused_row(a, r_end, n));
+    const int fresh = uniform(fused_row(a, r_end, n));
     const int r_cache = fresh >= 0 ? fresh : r_end;  // rows read from the cache
     const __amdgpu_buffer_rsrc_t kres = PAGED ? buffer_rsrc(a.k, a.pool_bytes) : buffer_rsrc(kbase, r_cache * (2 * D));
     const __amdgpu_buffer_rsrc_t vres = PAGED ? buffer_rsrc(a.v, a.pool_bytes) : buffer_rsrc(vbase, r_cache * (2 * D));
@@ -679,11 +679,33 @@ struct MfmaPiece {
       }
       __syncthreads();
     }
+    // Fused append through the table: the new row is attended from k_new /
+    // v_new and written after the loop, if its block's entry is valid; if
+    // not, it reads as zeros (the block's other rows too), as after
+    // kvc_paged_append (which skips such a sequence) and kvc_paged_decode_attn.
+    const int fresh_off =
+        (PAGED && fresh >= 0) ? uniform(sm.u.t.blk[(fresh >> shift) - blk0]) : kNoRow;  // pool byte offset
+    const bool patch = fresh >= 0 && (!PAGED || fresh_off != kNoRow);
     // Byte offset of row r of the tile at `base` (r < base + TR), given the
-    // offsets of the tile's first and second block.
+    // offsets of the tile's first and second block. (The new row's stale pool
+    // copy may be loaded; patch_tile replaces it before it is used.)
     auto paged_row = [&](int base, int r, int off0, int off1) {
       const int off = ((r >> shift) == (base >> shift)) ? off0 : off1;
       return r < r_end ? off + ((r & ((1 << shift) - 1)) * (2 * D)) : kNoRow;
+    };
+    // the lanes that hold the new row take it from k_new / v_new
+    auto patch_tile = [&](int base, bf16x8_t (&kr)[KS], u32x4_t (&vr)[VCH]) {
+      if (patch && fresh >= base && fresh < base + TR) {  // this tile holds the new row
+        if (base + j == fresh) {
+#pragma unroll
+          for (int k = 0; k < KS; ++k) kr[k] = *reinterpret_cast<const bf16x8_t*>(knew + 32 * k + 8 * g);
+        }
+#pragma unroll
+        for (int i = 0; i < VCH; ++i) {
+          const int f = i * 64 + lane;
+          if (base + f / CPR == fresh) vr[i] = *reinterpret_cast<const u32x4_t*>(vnew + 8 * (f % CPR));
+        }
+      }
     };
 
     auto load_tile = [&](int base, bf16x8_t (&kr)[KS], u32x4_t (&vr)[VCH]) {
@@ -702,6 +724,7 @@ struct MfmaPiece {
           const int vb = paged_row(base, base + f / CPR, off0, off1) + (f % CPR) * 16;
           vr[i] = __builtin_amdgcn_raw_buffer_load_b128(vres, vb, 0, 0);
         }
+        patch_tile(base, kr, vr);
         return;
       }
       const int kb = base * (2 * D) + koff;
@@ -711,17 +734,7 @@ struct MfmaPiece {
       const int vb = base * (2 * D) + voff;
 #pragma unroll
       for (int i = 0; i < VCH; ++i) vr[i] = __builtin_amdgcn_raw_buffer_load_b128(vres, vb + 1024 * i, 0, 0);
-      if (fresh >= base && fresh < base + TR) {  // this tile holds the new row
-        if (base + j == fresh) {
-#pragma unroll
-          for (int k = 0; k < KS; ++k) kr[k] = *reinterpret_cast<const bf16x8_t*>(knew + 32 * k + 8 * g);
-        }
-#pragma unroll
-        for (int i = 0; i < VCH; ++i) {
-          const int f = i * 64 + lane;
-          if (base + f / CPR == fresh) vr[i] = *reinterpret_cast<const u32x4_t*>(vnew + 8 * (f % CPR));
-        }
-      }
+      patch_tile(base, kr, vr);
     };
     auto use_tile = [&](int base, const bf16x8_t (&kr)[KS], const u32x4_t (&vr)[VCH]) {
       // stage V row-major in LDS
@@ -810,7 +823,20 @@ struct MfmaPiece {
       }
     }
 
-    if constexpr (!PAGED) fused_write<uint16_t, D>(a, b, kvg, chunk, fresh);
+    if constexpr (!PAGED) {
+      fused_write<uint16_t, D>(a, b, kvg, chunk, fresh);
+    } else if (patch && chunk == 0) {  // the new row into its block
+      uint8_t* kdst = reinterpret_cast<uint8_t*>(const_cast<void*>(a.k)) + fresh_off +
+                      (fresh & ((1 << shift) - 1)) * (2 * D);
+      uint8_t* vdst = reinterpret_cast<uint8_t*>(const_cast<void*>(a.v)) + fresh_off +
+                      (fresh & ((1 << shift) - 1)) * (2 * D);
+      for (int i = threadIdx.x; i < 2 * CPR; i += kThreads) {
+        const bool kk = i < CPR;
+        const int c = kk ? i : i - CPR;
+        const uint4 x = reinterpret_cast<const uint4*>(kk ? knew : vnew)[c];
+        reinterpret_cast<uint4*>(kk ? kdst : vdst)[c] = x;
+      }
+    }
     combine(a, sm, o, m, l, b, h0, whole, slot);
     return true;
   }
@@ -1356,7 +1382,7 @@ hipError_t kvc_launch_gqa_decode(const kvc_cache* c, const void* k_layer, const 
   a.table_width = c->table_width;
   a.pool_bytes = (int)c->kv_bytes;
   if (c->paged) {
-    if (!block_table || c->d.dtype != KVC_BF16 || k_new || c->table_width > KVC_MAX_TABLE ||
+    if (!block_table || c->d.dtype != KVC_BF16 || c->table_width > KVC_MAX_TABLE ||
         c->kv_bytes >= (1ull << 30))
       return hipErrorInvalidValue;
     switch (c->d.head_dim) {

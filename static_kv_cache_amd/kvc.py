@@ -61,6 +61,7 @@ _SIGS = {
     "kvc_alloc_paged": [ctypes.POINTER(Desc), _i32, _i32, _p, ctypes.POINTER(_p)],
     "kvc_paged_append": [_p, _i32, _p, _p, _p, _p, _i32, _p],
     "kvc_paged_decode_attn": [_p, _i32, _p, _p, _p, _p, _p, ctypes.c_float, _p],
+    "kvc_paged_append_decode_attn": [_p, _i32, _p, _p, _p, _p, _p, _p, ctypes.c_float, _p],
     "kvc_prefix_bytes": [_p, _p, ctypes.POINTER(ctypes.c_uint64)],
     "kvc_save_prefix": [_p, _p, _p, ctypes.c_uint64, _p],
     "kvc_load_prefix": [_p, _p, ctypes.c_uint64, _p, _p, _p],
@@ -478,6 +479,18 @@ class PagedCache(Cache):
         _call("kvc_paged_decode_attn", self.handle, layer, qp, op, self._table(block_table),
               self._idx(valid_lens, "valid_lens"), self._idx(cache_index, "cache_index"), float(sm_scale),
               _stream(self.device))
+
+
+    def paged_append_decode_attn(self, layer, k_new, v_new, q, out, block_table, cache_index, sm_scale):
+        """One launch: the new row at cache_index through the table, then attention over rows
+        [0, cache_index + 1) (kvc_paged_append_decode_attn)."""
+        d = self.desc
+        shape = (d.batch, d.n_kv_heads, 1, d.head_dim)
+        kp, vp = self._check(k_new, shape, name="k_new"), self._check(v_new, shape, name="v_new")
+        qp = self._check(q, (d.batch, d.n_heads, d.head_dim), name="q")
+        op = self._check(out, (d.batch, d.n_heads, d.head_dim), name="out")
+        _call("kvc_paged_append_decode_attn", self.handle, layer, kp, vp, qp, op, self._table(block_table),
+              self._idx(cache_index, "cache_index"), float(sm_scale), _stream(self.device))
 
 
 def _memcpy_d2d(dst, src, nbytes, device):

@@ -280,3 +280,94 @@ def test_paged_llama3_full_size_sampled():
         tol_check(got[b:b + 1], want, "bf16", f"sequence {b} (n={n})")
     cache.free()
     static.free()
+
+
+@pytest.mark.parametrize("B,H,Hkv,D,S,bs,wg", [
+    (4, 16, 4, 128, 1024, 16, 0),
+    (3, 8, 2, 64, 512, 32, 64),
+    (2, 32, 8, 128, 2048, 256, 0),
+    (5, 4, 1, 256, 256, 16, 7),
+])
+def test_paged_fused_equals_append_then_decode(B, H, Hkv, D, S, bs, wg):
+    """kvc_paged_append_decode_attn gives the output bits and pool bits of
+    kvc_paged_append followed by kvc_paged_decode_attn (same tables, same
+    grid), and the oracle's decode step within the bf16 bound. The new rows
+    fall at row 0, at block starts and ends, and mid-block."""
+    dev = device()
+    rng = np.random.default_rng(31 + D + bs + wg)
+    W = S // bs
+    nb = B * W + 5
+    say(f"paged fused: B={B} H={H} Hkv={Hkv} D={D} S={S} bs={bs} workgroups={wg}")
+    fused, ref = make(dev, B, H, Hkv, D, S, bs, nb)
+    two, _ = make(dev, B, H, Hkv, D, S, bs, nb)
+    table = random_tables(rng, B, W, nb)
+    tab = kvc.to_device(table, dev)
+    lens = [S, S // 2, 1, bs, bs + 1][:B]
+    k, v = fill_both(dev, fused, ref, rng, table, lens)
+    two.paged_append(0, kvc.to_device(k, dev), kvc.to_device(v, dev), tab,
+                     kvc.to_device(np.zeros(B, dtype=np.int32), dev))
+    if wg:
+        fused.set_workgroups(wg)
+        two.set_workgroups(wg)
+    ci = np.array([S - 1, S // 2, 0, bs - 1, bs][:B], dtype=np.int32)
+    kn = synthetic.draw(rng, (B, Hkv, 1, D), "bf16")
+    vn = synthetic.draw(rng, (B, Hkv, 1, D), "bf16")
+    q = synthetic.draw(rng, (B, H, D), "bf16")
+    knd, vnd, qd, cid = (kvc.to_device(x, dev) for x in (kn, vn, q, ci))
+    a = torch.empty((B, H, D), dtype=torch.bfloat16, device=dev)
+    b = torch.empty_like(a)
+    for rep in range(2):  # the second call reuses the cached split
+        fused.paged_append_decode_attn(0, knd, vnd, qd, a, tab, cid, 0.088)
+        fused.check()
+    two.paged_append(0, knd, vnd, tab, cid)
+    two.paged_decode_attn(0, qd, b, tab, cache_index=cid, sm_scale=0.088)
+    two.check()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16)), "fused output bits differ from the two calls"
+    assert ref.append(0, kn, vn, ci, table) == []
+    assert pools_equal(fused, ref), "fused pool differs from the oracle"
+    assert pools_equal(two, ref)
+    kg, vg = ref.gather(0, table, B)
+    tol_check(to_f64(a), oatt.decode_attention(q, kg, vg, list(ci + 1), 0.088), "bf16", "paged fused")
+    fused.free()
+    two.free()
+
+
+def test_paged_fused_skips_like_the_two_calls():
+    """A new row whose block entry lies outside the pool, and a cache_index
+    outside the capacity: the fused call writes nothing for them, raises the
+    flag, and gives the two calls' output bits (zeros for the second)."""
+    dev = device()
+    rng = np.random.default_rng(41)
+    B, H, Hkv, D, S, bs = 3, 8, 2, 128, 64, 16
+    nb = 12
+    table = np.array([[0, 1, 2, 3], [4, 5, -1, 6], [7, 8, 9, 10]], dtype=np.int32)
+    tab = kvc.to_device(table, dev)
+    fused, ref = make(dev, B, H, Hkv, D, S, bs, nb)
+    two, _ = make(dev, B, H, Hkv, D, S, bs, nb)
+    k = synthetic.draw(rng, (B, Hkv, 30, D), "bf16")
+    v = synthetic.draw(rng, (B, Hkv, 30, D), "bf16")
+    zero = kvc.to_device(np.zeros(B, dtype=np.int32), dev)
+    for c in (fused, two):  # rows 0..29; sequence 1 stops short of its bad block (rows 32..47)
+        c.paged_append(0, kvc.to_device(k, dev), kvc.to_device(v, dev), tab, zero)
+        c.check()
+    ci = np.array([20, 35, S + 3], dtype=np.int32)  # b = 1: new row in the bad block; b = 2: out of range
+    kn = kvc.to_device(synthetic.draw(rng, (B, Hkv, 1, D), "bf16"), dev)
+    vn = kvc.to_device(synthetic.draw(rng, (B, Hkv, 1, D), "bf16"), dev)
+    q = kvc.to_device(synthetic.draw(rng, (B, H, D), "bf16"), dev)
+    cid = kvc.to_device(ci, dev)
+    a = torch.empty((B, H, D), dtype=torch.bfloat16, device=dev)
+    b = torch.empty_like(a)
+    fused.paged_append_decode_attn(0, kn, vn, q, a, tab, cid, 0.1)
+    assert fused.check_status() == kvc.KVC_ERR_DEVICE_RANGE
+    two.paged_append(0, kn, vn, tab, cid)
+    two.paged_decode_attn(0, q, b, tab, cache_index=cid, sm_scale=0.1)
+    assert two.check_status() == kvc.KVC_ERR_DEVICE_RANGE
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert torch.count_nonzero(a[2].float()) == 0
+    fk, fv = fused.layer_tensors(0)
+    tk, tv = two.layer_tensors(0)
+    assert torch.equal(fk.view(torch.int16), tk.view(torch.int16))
+    assert torch.equal(fv.view(torch.int16), tv.view(torch.int16))
+    del fk, fv, tk, tv
+    fused.free()
+    two.free()
