@@ -161,6 +161,8 @@ def test_paged_calls_reject_null_handles(lib):
     z = ctypes.c_void_p(16)
     assert lib.kvc_paged_append(None, 0, z, z, z, z, 1, None) == kvc.KVC_ERR_INVALID_ARG
     assert lib.kvc_paged_decode_attn(None, 0, z, z, z, z, z, ctypes.c_float(0.1), None) == kvc.KVC_ERR_INVALID_ARG
+    assert (lib.kvc_paged_append_decode_attn(None, 0, z, z, z, z, z, z, ctypes.c_float(0.1), None)
+            == kvc.KVC_ERR_INVALID_ARG)
     assert lib.kvc_bytes_paged(None, 16, 4, ctypes.byref(ctypes.c_uint64())) == kvc.KVC_ERR_INVALID_ARG
     assert lib.kvc_alloc_paged(None, 16, 4, None, None) == kvc.KVC_ERR_INVALID_ARG
 
