@@ -401,8 +401,10 @@ struct ValuPiece {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int rc = min(base + u * RPI + rs, r_end - 1);
-        kr[u] = kp[(size_t)rc * LPR];
-        vr[u] = vp[(size_t)rc * LPR];
+        kr[u] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kp) +
+                                                                     (size_t)rc * LPR));
+        vr[u] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vp) +
+                                                                     (size_t)rc * LPR));
       }
       // rows at or past `fresh` clamp to it: every such lane takes the new
       // row (the cache row is stale until this launch writes it)
@@ -717,12 +719,12 @@ struct MfmaPiece {
         const int kb = paged_row(base, base + j, off0, off1) + 16 * g;
 #pragma unroll
         for (int k = 0; k < KS; ++k)
-          kr[k] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(kres, kb + 64 * k, 0, 0));
+          kr[k] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(kres, kb + 64 * k, 0, kStreamLoad));
 #pragma unroll
         for (int i = 0; i < VCH; ++i) {
           const int f = i * 64 + lane;
           const int vb = paged_row(base, base + f / CPR, off0, off1) + (f % CPR) * 16;
-          vr[i] = __builtin_amdgcn_raw_buffer_load_b128(vres, vb, 0, 0);
+          vr[i] = __builtin_amdgcn_raw_buffer_load_b128(vres, vb, 0, kStreamLoad);
         }
         patch_tile(base, kr, vr);
         return;
@@ -730,10 +732,10 @@ struct MfmaPiece {
       const int kb = base * (2 * D) + koff;
 #pragma unroll
       for (int k = 0; k < KS; ++k)
-        kr[k] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(kres, kb + 64 * k, 0, 0));
+        kr[k] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(kres, kb + 64 * k, 0, kStreamLoad));
       const int vb = base * (2 * D) + voff;
 #pragma unroll
-      for (int i = 0; i < VCH; ++i) vr[i] = __builtin_amdgcn_raw_buffer_load_b128(vres, vb + 1024 * i, 0, 0);
+      for (int i = 0; i < VCH; ++i) vr[i] = __builtin_amdgcn_raw_buffer_load_b128(vres, vb + 1024 * i, 0, kStreamLoad);
       patch_tile(base, kr, vr);
     };
     auto use_tile = [&](int base, const bf16x8_t (&kr)[KS], const u32x4_t (&vr)[VCH]) {
@@ -1008,12 +1010,12 @@ struct I8Piece {
     auto load_tile = [&](int base, Tile& tl) {
       const int kb = base * D + koff;
 #pragma unroll
-      for (int i = 0; i < KL; ++i) tl.k[i] = __builtin_amdgcn_raw_buffer_load_b128(kres, kb + 16 * i, 0, 0);
+      for (int i = 0; i < KL; ++i) tl.k[i] = __builtin_amdgcn_raw_buffer_load_b128(kres, kb + 16 * i, 0, kStreamLoad);
       const int vb = base * D + voff;
 #pragma unroll
-      for (int i = 0; i < VL; ++i) tl.v[i] = __builtin_amdgcn_raw_buffer_load_b128(vres, vb + 1024 * i, 0, 0);
-      tl.sk = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ksres, (base + 4 * g) * 4, 0, 0));
-      tl.sv = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(vsres, (base + 4 * g) * 4, 0, 0));
+      for (int i = 0; i < VL; ++i) tl.v[i] = __builtin_amdgcn_raw_buffer_load_b128(vres, vb + 1024 * i, 0, kStreamLoad);
+      tl.sk = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ksres, (base + 4 * g) * 4, 0, kStreamLoad));
+      tl.sv = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(vsres, (base + 4 * g) * 4, 0, kStreamLoad));
     };
     auto use_tile = [&](int base, const Tile& tile, auto patch_tag) {
       constexpr bool kPatch = decltype(patch_tag)::value;  // the piece holds the new row

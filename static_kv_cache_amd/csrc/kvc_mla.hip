@@ -130,7 +130,7 @@ __device__ __forceinline__ void mla_piece(const MlaArgs& a, unsigned char* tiles
   auto load = [&](u32x4_t (&st)[kVec], int t0) {
     const int off = t0 * kRowBytes + (int)threadIdx.x * 16;
 #pragma unroll
-    for (int i = 0; i < kVec; ++i) st[i] = __builtin_amdgcn_raw_buffer_load_b128(res, off + i * 16 * kThreads, 0, 0);
+    for (int i = 0; i < kVec; ++i) st[i] = __builtin_amdgcn_raw_buffer_load_b128(res, off + i * 16 * kThreads, 0, kStreamLoad);
   };
   auto stage = [&](unsigned char* tile, const u32x4_t (&st)[kVec]) {
 #pragma unroll
