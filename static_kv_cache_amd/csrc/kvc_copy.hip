@@ -90,6 +90,8 @@ __global__ __launch_bounds__(256) void paged_rows_kernel(
 // n_b rows of every kv head of (b, layer, kv) are one run in the cache per
 // head ([S] rows apart) and one packed run in the image, copied as units of
 // U (16-byte vectors for rows, 4-byte words for int8 scales).
+typedef uint32_t vec4u __attribute__((ext_vector_type(4)));  // 16-byte unit (a vector type for nt loads)
+
 template <typename U>
 __global__ __launch_bounds__(256) void prefix_copy_kernel(U* __restrict__ cache, U* __restrict__ image,
                                                           const int32_t* __restrict__ map, bool save,
@@ -107,12 +109,26 @@ __global__ __launch_bounds__(256) void prefix_copy_kernel(U* __restrict__ cache,
   const long long units = run * groups;
   U* cb = cache + layer * layer_units + kv * kv_units + (long long)b * groups * max_context * row_units;
   U* ib = image + ((long long)lk * total_rows + first) * groups * row_units;
+  // every unit is read once and written once: non-temporal on both sides
+  auto move = [&](U* cp, U* ip) {
+    if (save)
+      __builtin_nontemporal_store(__builtin_nontemporal_load(cp), ip);
+    else
+      __builtin_nontemporal_store(__builtin_nontemporal_load(ip), cp);
+  };
+  if (units < (1LL << 31)) {  // 32-bit index arithmetic (the usual case)
+    const uint32_t run32 = (uint32_t)run;
+    for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < (uint32_t)units; i += gridDim.x * 256u) {
+      const uint32_t g = i / run32;
+      const uint32_t rem = i - g * run32;
+      move(cb + (long long)g * max_context * row_units + rem, ib + (long long)g * run + rem);
+    }
+    return;
+  }
   for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < units; i += (long long)gridDim.x * 256) {
     const int g = (int)(i / run);
     const long long rem = i - g * run;
-    U* cp = cb + (long long)g * max_context * row_units + rem;
-    U* ip = ib + g * run + rem;
-    if (save) *ip = *cp; else *cp = *ip;
+    move(cb + (long long)g * max_context * row_units + rem, ib + g * run + rem);
   }
 }
 
@@ -132,8 +148,8 @@ hipError_t kvc_launch_prefix_copy(uint8_t* cache, uint8_t* image, const int32_t*
   if (gx > 65535) gx = 65535;
   const dim3 grid((unsigned)gx, (unsigned)batch, (unsigned)(n_layers * kv_parts));
   if (unit_bytes == 16)
-    prefix_copy_kernel<uint4><<<grid, dim3(256), 0, stream>>>(
-        (uint4*)cache, (uint4*)image, map, save, (long long)(layer_bytes / 16), (long long)(kv_bytes / 16), kv_parts,
+    prefix_copy_kernel<vec4u><<<grid, dim3(256), 0, stream>>>(
+        (vec4u*)cache, (vec4u*)image, map, save, (long long)(layer_bytes / 16), (long long)(kv_bytes / 16), kv_parts,
         groups, max_context, row_units, total_rows);
   else if (unit_bytes == 4)
     prefix_copy_kernel<uint32_t><<<grid, dim3(256), 0, stream>>>(
