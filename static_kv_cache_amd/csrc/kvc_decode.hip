@@ -1202,7 +1202,14 @@ void gqa_decode_kernel(DecodeArgs a) {
   const int HC = a.n_kv_heads * a.head_chunks;  // segments per sequence
   const int32_t* entry = plan_entry(a.plan);
   const bool key = plan_key(a.plan, a.n_wg, min_rows, B);
-  const int count = uniform(key ? entry[0] : -1);  // pieces in this workgroup's cached entry
+  const int entry_count = entry[0];  // requested with the header, whatever the key
+  const int count = uniform(key ? entry_count : -1);  // pieces in this workgroup's cached entry
+  // The first cached piece's fields, requested now so that their latency
+  // overlaps the length scan below (read before it, the first loads of wave
+  // 0, and with them every wave's gate, waited for both in turn).
+  int first[kPieceInts];
+#pragma unroll
+  for (int i = 0; i < kPieceInts; ++i) first[i] = entry[1 + i];
   if (t < 64) {
     scan_lengths(a.valid_lens, a.cache_index, B, a.max_context, kSegRows, s_prefix, &s_umax, a.err_flag,
                  blockIdx.x == 0, min_rows, a.plan + KVC_PLAN_LENS, &st.gate);
@@ -1219,8 +1226,11 @@ void gqa_decode_kernel(DecodeArgs a) {
     bool planned = true;
     for (int k = 0; k < count; ++k) {
       const int32_t* pc = entry + 1 + k * kPieceInts;
-      const int b = uniform(pc[0]), hc = uniform(pc[1]), r_begin = uniform(pc[2]), r_end = uniform(pc[3]);
-      const int n = uniform(pc[4]);
+      int f[kPieceInts];
+#pragma unroll
+      for (int i = 0; i < kPieceInts; ++i) f[i] = k == 0 ? first[i] : pc[i];
+      const int b = uniform(f[0]), hc = uniform(f[1]), r_begin = uniform(f[2]), r_end = uniform(f[3]);
+      const int n = uniform(f[4]);
       const long long s = (long long)b * HC + hc;
       const bool whole = r_begin == 0 && r_end == n;
       const int kvg = hc / a.head_chunks;
@@ -1236,8 +1246,8 @@ void gqa_decode_kernel(DecodeArgs a) {
           split[nsplit].n = n;
           split[nsplit].b = b;
           split[nsplit].h0 = kvg * (a.n_heads / a.n_kv_heads) + chunk * a.chunk_heads;
-          split[nsplit].w0 = pc[5];
-          split[nsplit].np = pc[6];
+          split[nsplit].w0 = f[5];
+          split[nsplit].np = f[6];
         }
         ++nsplit;
       }

@@ -223,7 +223,10 @@ struct PlanState {
 // Whether the header names this launch's grid, append mode and batch (the
 // lengths are compared by scan_lengths). Uniform: every wave reads it.
 __device__ __forceinline__ bool plan_key(const int32_t* plan, int n_wg, int min_rows, int B) {
-  return plan[0] == 1 && plan[1] == n_wg && plan[2] == min_rows && plan[3] == B;
+  // the four header words in one load, compared without short-circuit
+  // branches (which made them four dependent loads at the kernel's start)
+  const int4 h = *reinterpret_cast<const int4*>(plan);
+  return (h.x == 1) & (h.y == n_wg) & (h.z == min_rows) & (h.w == B);
 }
 
 // This workgroup's cached entry.
