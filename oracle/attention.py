@@ -102,14 +102,28 @@ def prefill_attention(q, k_cache, v_cache, start, sm_scale):
     start); "10.3 - KV cache implementation details", section 3: query i of
     the chunk (position start + i) attends positions 0 .. start + i.
     q: [B, H, t, D]; k_cache, v_cache: [B, H_kv, S, D] holding rows
-    [0, start + t). Each query is the decode of that position with valid
-    length start + i + 1. Returns float64 [B, H, t, D].
+    [0, start + t). Written as the masked matrix form of that definition:
+    for each (b, h), scores = sm_scale * Q K^T over the n = start + t rows,
+    entries with key position > query position removed (weight 0), a
+    row-wise softmax and the product with V; each row is then the decode of
+    its position with valid length start + i + 1. Returns float64 [B, H, t, D].
     """
     q = widen(q)
     B, H, t, D = q.shape
+    H_kv = k_cache.shape[1]
+    group = H // H_kv
+    n = start + t
+    allowed = np.arange(n)[None, :] <= (start + np.arange(t))[:, None]   # [t, n]
     out = np.zeros((B, H, t, D), dtype=np.float64)
-    for i in range(t):
-        out[:, :, i] = decode_attention(q[:, :, i], k_cache, v_cache, np.full(B, start + i + 1), sm_scale)
+    for b in range(B):
+        for g in range(H_kv):
+            keys = widen(k_cache[b, g, :n])      # [n, D]; rows >= n never touched
+            vals = widen(v_cache[b, g, :n])
+            for h in range(g * group, (g + 1) * group):
+                scores = np.where(allowed, sm_scale * (q[b, h] @ keys.T), -np.inf)
+                m = np.max(scores, axis=1, keepdims=True)
+                p = np.exp(scores - m)              # exp(-inf) = 0 for the removed entries
+                out[b, h] = (p @ vals) / np.sum(p, axis=1, keepdims=True)
     return out
 
 

@@ -55,11 +55,7 @@ using namespace kvcd;
 
 constexpr float kLazy = 8.0f;  // log2 headroom before the running maximum is moved (VALU piece)
 constexpr float kLazyMfma = 64.0f;  // the same for the matrix-core piece (fp32 sums, bf16 P)
-#ifndef KVC_WAVES
 constexpr int kWaves = 4;      // waves per workgroup
-#else
-constexpr int kWaves = KVC_WAVES;
-#endif
 constexpr int kThreads = 64 * kWaves;
 
 template <typename T>
@@ -138,7 +134,6 @@ struct DecodeArgs {
   int head_chunks;             // chunks per kv head's query group
   int chunk_heads;             // query heads per chunk (group / head_chunks)
   int n_wg;                    // persistent grid size (launched)
-  int n_cus, wa, wb;           // partition weights: first n_cus workgroups wa, the rest wb
   float* ws_acc;               // [slot][GC][D]
   float* ws_ml;                // [slot][GC][2]
   int32_t* ws_cnt;             // [B * H_kv * chunks] arrival counters (self-resetting)
@@ -190,21 +185,9 @@ __device__ __forceinline__ void fused_write(const DecodeArgs& a, int b, int g, i
 // of its real ones, so a workgroup whose range crosses into another segment
 // is handed correspondingly fewer real rows and all workgroups finish
 // together. Virtual rows map to no work.
-#ifndef KVC_SEG_ROWS
 constexpr int kSegRows = 256;  // measured: 0 / 128 / 192 / 256 / 384 -> 35.1 / 33.9 / 33.5 / 33.3 / 33.9 us
-#else
-constexpr int kSegRows = KVC_SEG_ROWS;
-#endif
 static_assert(kSegRows >= 0 && kSegRows <= kMaxSegRows, "row space must stay below 2^31");
 
-// Row-space shares of the first workgroup on each CU and of the others.
-#ifndef KVC_SHARE_FIRST
-constexpr int kShareFirst = 1;
-constexpr int kShareRest = 1;
-#else
-constexpr int kShareFirst = KVC_SHARE_FIRST;
-constexpr int kShareRest = KVC_SHARE_REST;
-#endif
 
 // A piece that is part of a segment (only a workgroup's first and last
 // piece can be) is recorded while the workgroup streams on; at the end the
@@ -218,9 +201,7 @@ struct SplitPiece {
   int w0, np;  // the segment's first workgroup and number of pieces
 };
 
-#ifndef KVC_MERGE_WIDE
-#define KVC_MERGE_WIDE 16  // pieces per round of loads when a segment has more than 8 (32 measured the same)
-#endif
+constexpr int kMergeWide = 16;  // pieces per round of loads when a segment has more than 8 (32 measured the same)
 
 // The merged output dims d .. d + 3 of head h of segment s, whose np pieces
 // sit in slots w0 + s .. w0 + s + np - 1, in batches of K pieces.
@@ -291,7 +272,7 @@ __device__ void finish_splits(const DecodeArgs& a, const SplitPiece* sp, int nsp
         const int h = vi / DV;
         const int d = 4 * (vi - h * DV);
         float x[4];
-        merge_group<D, SH, KVC_MERGE_WIDE>(a, q.s, w0, np, h, d, x);
+        merge_group<D, SH, kMergeWide>(a, q.s, w0, np, h, d, x);
         if (v0 + (int)threadIdx.x < gc * DV) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) store_out(o + h * D + d + e, x[e]);
@@ -345,11 +326,7 @@ struct ValuPiece {
   static constexpr int EPV = Storage<T>::kEPV;  // elements per 16-byte vector
   static constexpr int LPR = D / EPV;           // lanes per cached row
   static constexpr int RPI = 64 / LPR;          // rows per wave instruction (row slots)
-#ifndef KVC_TILE_U
   static constexpr int U = (GC >= 8) ? 2 : 4;   // row vectors per K (and V) per tile and lane
-#else
-  static constexpr int U = KVC_TILE_U;
-#endif
   static constexpr int TILE = RPI * U;          // rows per wave per tile
   static_assert(LPR >= 1 && LPR <= 64 && 64 % LPR == 0, "row must map onto a wave");
 
@@ -591,11 +568,7 @@ struct MfmaPiece {
   static constexpr int CPR = D / 8;            // 16-byte chunks per row
   static constexpr int VCH = TR * CPR / 64;    // V chunks per lane per tile
   static constexpr int VSTRIDE = 2 * D + 32;   // bytes per staged V row (skew spreads LDS banks)
-#ifdef KVC_MFMA_NBUF
-  static constexpr int NBUF = KVC_MFMA_NBUF;
-#else
   static constexpr int NBUF = D <= 64 ? 3 : 2; // register tiles in the ring (register budget)
-#endif
   static_assert(D % 32 == 0 && VCH >= 1 && TR * CPR % 64 == 0, "head_dim must be 32..256");
   static constexpr int kTable = PAGED ? KVC_MAX_TABLE : 1;
 
@@ -773,15 +746,15 @@ struct MfmaPiece {
         m = mn;
       }
       const float nm = (m == -INFINITY) ? 0.0f : -m;
-      float p[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        p[t] = __builtin_amdgcn_exp2f(fmaf(s[t], scale_log2, nm));
-        l += p[t];
-      }
+      // P rounded to bf16 for the product; the denominator sums the same
+      // rounded weights, so the output is a convex combination of V rows
       s16x4_t pa;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) pa[t] = __builtin_bit_cast(short, (__bf16)p[t]);
+      for (int t = 0; t < 4; ++t) {
+        const __bf16 pb = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[t], scale_log2, nm));
+        pa[t] = __builtin_bit_cast(short, pb);
+        l += (float)pb;
+      }
       // p.v: B operand = V[base + 4g + t][16 nb + j] by one transpose read
       const unsigned char* vrow = vs + (4 * g + (j >> 2)) * VSTRIDE + 8 * (j & 3);
 #pragma unroll
@@ -1183,11 +1156,7 @@ struct I8Piece {
 
 // Persistent decode kernel: grid = W workgroups of 256 threads.
 template <class P>
-__global__ __launch_bounds__(kThreads)
-#ifdef KVC_WAVES_PER_EU
-__attribute__((amdgpu_waves_per_eu(KVC_WAVES_PER_EU, KVC_WAVES_PER_EU)))
-#endif
-void gqa_decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads) void gqa_decode_kernel(DecodeArgs a) {
   __shared__ typename P::Smem sm;
   __shared__ int32_t s_prefix[KVC_MAX_BATCH + 1];
   __shared__ int32_t s_umax;  // longest segment in virtual rows
@@ -1270,7 +1239,7 @@ void gqa_decode_kernel(DecodeArgs a) {
     }
   }
 
-  const Partition part(R, a.n_wg, s_umax, a.n_cus, a.wa, a.wb);
+  const Partition part(R, a.n_wg, s_umax);
   int recorded = 0;  // pieces in this workgroup's new entry (thread 0)
   if (w < part.W) {
     const long long x = part.lo(w);
@@ -1311,9 +1280,6 @@ hipError_t launch_piece(const kvc_cache* c, DecodeArgs a, int chunk_heads, hipSt
   // pieces, two for the int8 piece where its registers allow; see there).
   a.n_wg = c->workgroups_forced > 0 ? c->workgroups_forced : c->num_cus * P::kWgPerCu;
   if (a.n_wg > c->max_workgroups) a.n_wg = c->max_workgroups;
-  a.n_cus = c->num_cus;
-  a.wa = kShareFirst;
-  a.wb = kShareRest;
   gqa_decode_kernel<P><<<dim3(a.n_wg), dim3(kThreads), 0, stream>>>(a);
   return hipGetLastError();
 }

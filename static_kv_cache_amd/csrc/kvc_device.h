@@ -104,33 +104,25 @@ constexpr int kMaxMerge = kMaxSpan + 2;    // pieces of one segment, at most
 constexpr int kMinRowsPerWorkgroup = 64;   // and every workgroup gets >= 64 rows (no empty ranges)
 constexpr int kMaxSegRows = 1024;          // start-up rows allowed (the desc limits keep R < 2^31)
 
-// The split of the row space among the persistent workgroups. Workgroups
-// [0, C) (C = CUs: the first workgroup on each CU, which the CU favours when
-// it issues) take shares of weight wa, the rest shares of weight wb; with
-// wa = wb every workgroup takes R / W rows. Workgroup w takes
-// [lo(w), lo(w + 1)). The grid is capped so that even the narrowest share
-// has >= kMinRowsPerWorkgroup rows and >= 1/kMaxSpan of the longest segment
-// (u_max virtual rows), so a segment is cut into at most kMaxMerge pieces.
+// The split of the row space among the persistent workgroups: workgroup w
+// takes [lo(w), lo(w + 1)) with lo(w) = R w / W. The grid is capped so that
+// every share has >= kMinRowsPerWorkgroup rows and >= 1/kMaxSpan of the
+// longest segment (u_max virtual rows), so a segment is cut into at most
+// kMaxMerge pieces.
 struct Partition {
   long long R;
-  int W, C, wa, wb;
+  int W;
 
-  __device__ __forceinline__ Partition(long long R_, int n_wg, int u_max, int C_, int wa_, int wb_)
-      : R(R_), W(1), C(C_), wa(wa_), wb(wb_) {
-    const long long narrow = R * min(wa, wb) / max(wa, wb);  // R as seen by the narrowest share
+  __device__ __forceinline__ Partition(long long R_, int n_wg, int u_max) : R(R_), W(1) {
     long long w = n_wg;
-    w = min(w, max(1LL, narrow * kMaxSpan / max(u_max, 1)));
-    w = min(w, max(1LL, narrow / kMinRowsPerWorkgroup));
+    w = min(w, max(1LL, R * kMaxSpan / max(u_max, 1)));
+    w = min(w, max(1LL, R / kMinRowsPerWorkgroup));
     W = (int)w;
   }
-  __device__ __forceinline__ long long cum(int w) const {
-    return w <= C ? (long long)w * wa : (long long)C * wa + (long long)(w - C) * wb;
-  }
-  __device__ __forceinline__ long long lo(int w) const { return w >= W ? R : R * cum(w) / cum(W); }
+  __device__ __forceinline__ long long lo(int w) const { return w >= W ? R : R * w / W; }
   // Workgroup whose range contains row x.
   __device__ __forceinline__ int of(long long x) const {
-    const long long c = x * cum(W) / R;  // cumulative weight at x
-    int w = c <= (long long)C * wa ? (int)(c / wa) : C + (int)((c - (long long)C * wa) / wb);
+    int w = (int)(x * W / R);
     w = min(max(w, 0), W - 1);
     while (w + 1 < W && lo(w + 1) <= x) ++w;
     while (w > 0 && lo(w) > x) --w;

@@ -68,13 +68,6 @@ constexpr int kSegRowsMla = 160;             // start-up rows of a segment (see 
 constexpr float kLazyMfma = 64.0f;           // log2 headroom before the reference maximum moves
 static_assert(kTok * kRowBytes % (16 * kThreads) == 0, "tile must split evenly over the threads");
 static_assert(kSegRowsMla <= kMaxSegRows, "row space must stay below 2^31");
-#ifndef KVC_SHARE_FIRST
-constexpr int kShareFirstMla = 1;            // row-space shares of the first workgroup on each CU
-constexpr int kShareRestMla = 1;             // and of the others
-#else
-constexpr int kShareFirstMla = KVC_SHARE_FIRST;
-constexpr int kShareRestMla = KVC_SHARE_REST;
-#endif
 
 struct MlaArgs {
   const uint16_t* rows;        // layer rows [B][S][576]
@@ -88,7 +81,6 @@ struct MlaArgs {
   int batch, n_heads, max_context;
   int head_chunks, chunk_heads;  // H = head_chunks * chunk_heads, chunk_heads <= 16
   int n_wg;
-  int n_cus, wa, wb;           // partition weights: first n_cus workgroups wa, the rest wb
   int32_t* err_flag;
   int32_t* seg_info;           // [B * head_chunks][2]: first workgroup and pieces of each non-empty segment
 };
@@ -206,9 +198,9 @@ __device__ __forceinline__ void mla_piece(const MlaArgs& a, unsigned char* tiles
     bf16x8_t pa;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(s[u >> 2][u & 3], scale_log2, nm));
-      l += p;
-      pa[u] = (__bf16)p;
+      // the denominator sums the bf16 weights that enter the product
+      pa[u] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[u >> 2][u & 3], scale_log2, nm));
+      l += (float)pa[u];
     }
     // p.v over this wave's latent columns [128 wave, 128 wave + 128): B = the
     // rows 4g + t of both blocks by one transpose read per block
@@ -290,7 +282,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                   blockIdx.x == 0);
   const int HC = a.head_chunks;
   const long long R = (long long)s_prefix[B] * HC;
-  const Partition part(R, a.n_wg, s_umax, a.n_cus, a.wa, a.wb);
+  const Partition part(R, a.n_wg, s_umax);
   const int w = blockIdx.x;
   if (w >= part.W) return;
   const long long x = part.lo(w);
@@ -510,9 +502,6 @@ hipError_t kvc_launch_mla_attn(const kvc_cache* c, const void* rows_layer, const
   a.head_chunks = c->d.n_heads / a.chunk_heads;
   a.n_wg = c->workgroups_forced > 0 ? c->workgroups_forced : c->num_cus;  // one per CU (measured best)
   if (a.n_wg > c->max_workgroups) a.n_wg = c->max_workgroups;
-  a.n_cus = c->num_cus;
-  a.wa = kShareFirstMla;
-  a.wb = kShareRestMla;
   a.err_flag = c->err_flag;
   a.seg_info = c->ws_seg;
   mla_split_kernel<<<dim3(a.n_wg), dim3(kThreads), 0, stream>>>(a);

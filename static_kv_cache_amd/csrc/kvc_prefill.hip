@@ -43,12 +43,8 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kKeys = 32;                 // keys per tile
 constexpr float kLazy = 64.0f;            // log2 headroom before the reference maximum moves
-#ifndef KVC_PREFILL_QG
-#define KVC_PREFILL_QG 1                  // query groups of 16 per wave (1 measured best)
-#endif
-#ifndef KVC_PREFILL_NPF
-#define KVC_PREFILL_NPF 1                 // K/V tiles in flight in registers (1 measured best)
-#endif
+constexpr int kQueryGroups = 1;           // query groups of 16 per wave (1 measured best)
+constexpr int kTilesInFlight = 1;         // K/V tiles in flight in registers (1 measured best)
 
 struct PrefillArgs {
   const uint16_t* k;      // layer keys [B][H_kv][S][D]
@@ -129,7 +125,7 @@ __global__ __launch_bounds__(kThreads) void prefill_attn_kernel(PrefillArgs a) {
 
   // tile staging: thread t moves 16-byte vectors t + 256 i of the K and V
   // tiles; a ring of NPF register tiles keeps the next NPF tiles in flight
-  constexpr int NPF = KVC_PREFILL_NPF;
+  constexpr int NPF = kTilesInFlight;
   u32x4_t kr[NPF][P::VEC], vr[NPF][P::VEC];
   auto load = [&](int k0, u32x4_t (&kd)[P::VEC], u32x4_t (&vd)[P::VEC]) {
 #pragma unroll
@@ -201,9 +197,10 @@ __global__ __launch_bounds__(kThreads) void prefill_attn_kernel(PrefillArgs a) {
         const float nm = (m[qg] == -INFINITY) ? 0.0f : -m[qg];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sc[u], scale_log2, nm));
-          l[qg] += p;
-          pa[qg][u] = __builtin_bit_cast(short, (__bf16)p);
+          // the denominator sums the bf16 weights that enter the product
+          const __bf16 pb = (__bf16)__builtin_amdgcn_exp2f(fmaf(sc[u], scale_log2, nm));
+          l[qg] += (float)pb;
+          pa[qg][u] = __builtin_bit_cast(short, pb);
         }
       }
       // p.v: B operand = V[kb0 + 4g + u][16 nb + j] by one transpose read, shared by the groups
@@ -258,7 +255,7 @@ hipError_t kvc_launch_prefill_attn(const kvc_cache* c, const void* k_layer, cons
   const int G = a.n_heads / a.n_kv_heads;
   a.hpw = G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1);
   // query groups of 16 per wave: each K/V read from LDS feeds QG x the products
-  constexpr int QG = KVC_PREFILL_QG;
+  constexpr int QG = kQueryGroups;
   const int span = 64 * QG / a.hpw;
   a.n_qblocks = (t + span - 1) / span;
   const long long nx = (long long)c->d.batch * (a.n_heads / a.hpw);

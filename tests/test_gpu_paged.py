@@ -243,9 +243,9 @@ def test_paged_and_static_calls_do_not_mix():
     static.free()
 
 
-def test_paged_llama3_full_size_sampled():
+def test_paged_llama3_full_size():
     """Llama-3-8B-shaped decode (B=16, H=32, H_kv=8, d_h=128, S=4096) through block tables of
-    16-row blocks scattered over the pool, lengths ~U[1024, 4096]: sampled sequences against the
+    16-row blocks scattered over the pool, lengths ~U[1024, 4096]: every output against the
     oracle, and all of them bit-equal to the static decode."""
     dev = device()
     rng = np.random.default_rng(4096)
@@ -273,11 +273,9 @@ def test_paged_llama3_full_size_sampled():
     static.decode_attn(0, kvc.to_device(q, dev), ref_out, valid_lens=valid, sm_scale=scale)
     static.check()
     assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16))
-    got = to_f64(out)
-    for b in (0, int(np.argmax(lens)), B - 1):
-        n = int(lens[b])
-        want = oatt.decode_attention(q[b:b + 1], k[b:b + 1], v[b:b + 1], [n], scale)
-        tol_check(got[b:b + 1], want, "bf16", f"sequence {b} (n={n})")
+    want = oatt.decode_attention(q, k, v, lens, scale)
+    err = tol_check(to_f64(out), want, "bf16", "paged, every sequence")
+    say(f"  max abs err {err:.3e}")
     cache.free()
     static.free()
 

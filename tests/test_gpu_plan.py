@@ -78,3 +78,35 @@ def test_fused_and_plain_calls_interleaved():
     for i in range(6):
         assert torch.equal(outs[i].view(torch.int16), outs[0].view(torch.int16)), i
     cache.free()
+
+
+@pytest.mark.parametrize("workgroups", [16, 64])
+def test_overflowing_plan_entries(workgroups):
+    """Many short sequences on a small grid: a workgroup's range then holds more pieces than its
+    cached entry keeps (8), so those workgroups work their pieces out again on every call while
+    the others take theirs from the cache (with one long sequence, some workgroups hold a single
+    piece of it and keep their entries). Repeated calls give identical bits, and every call
+    matches the oracle, also after the lengths change."""
+    dev = device()
+    B, H, Hkv, D, S = 256, 8, 2, 64, 512
+    cache, ref, q, rng = setup(dev, B, H, Hkv, D, S, 23)
+    qd = kvc.to_device(q, dev)
+    cache.set_workgroups(workgroups)
+    short = rng.integers(1, 41, size=B).astype(np.int32)
+    short[7] = S  # one long sequence among them
+    changed = short.copy()
+    changed[::3] += 1
+    seen = {}
+    for lens in (short, short, changed, short, changed, changed):
+        key = lens.tobytes()
+        say(f"overflowing entries: workgroups {workgroups}, sum of lengths {int(lens.sum())}")
+        out = torch.empty((B, H, D), dtype=torch.bfloat16, device=dev)
+        cache.decode_attn(0, qd, out, valid_lens=kvc.to_device(lens, dev), sm_scale=0.125)
+        cache.check()
+        if key in seen:
+            assert torch.equal(out.view(torch.int16), seen[key].view(torch.int16))
+        else:
+            tol_check(to_f64(out), oatt.decode_attention(q, ref.keys(0), ref.values(0), lens, 0.125), "bf16",
+                      f"workgroups {workgroups}")
+            seen[key] = out
+    cache.free()

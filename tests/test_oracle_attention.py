@@ -122,3 +122,18 @@ def test_prefill_attention_equals_nocache_causal():
                                         torch.from_numpy(att.repeat_kv_heads(v[:, :, :7], 2)), is_causal=True,
                                         scale=0.3).numpy()
     assert np.allclose(att.prefill_attention(q[:, :, :7], k, v, 0, 0.3), sd, rtol=0, atol=1e-12)
+
+
+def test_prefill_attention_rows_are_decodes():
+    """Every row of the prefill equals the decode of its position (valid length start + i + 1),
+    GQA with groups of 3, chunks after cached rows and a one-token chunk."""
+    rng = np.random.default_rng(32)
+    B, H, Hkv, D, S = 2, 6, 2, 16, 40
+    k = rng.standard_normal((B, Hkv, S, D))
+    v = rng.standard_normal((B, Hkv, S, D))
+    for start, t in ((0, 40), (13, 9), (39, 1)):
+        q = rng.standard_normal((B, H, t, D))
+        got = att.prefill_attention(q, k, v, start, 0.25)
+        for i in range(t):
+            want = att.decode_attention(q[:, :, i], k, v, np.full(B, start + i + 1), 0.25)
+            assert np.allclose(got[:, :, i], want, rtol=0, atol=1e-12), (start, t, i)
