@@ -185,7 +185,7 @@ __device__ __forceinline__ void fused_write(const DecodeArgs& a, int b, int g, i
 // of its real ones, so a workgroup whose range crosses into another segment
 // is handed correspondingly fewer real rows and all workgroups finish
 // together. Virtual rows map to no work.
-constexpr int kSegRows = 256;  // measured: 0 / 128 / 192 / 256 / 384 -> 35.1 / 33.9 / 33.5 / 33.3 / 33.9 us
+constexpr int kSegRows = 192;  // measured (two pieces streamed as one): 0 / 64 / 128 / 192 / 256 -> 33.9 / 32.9 / 32.5 / 32.4 / 32.6 us
 static_assert(kSegRows >= 0 && kSegRows <= kMaxSegRows, "row space must stay below 2^31");
 
 
@@ -240,7 +240,7 @@ __device__ __forceinline__ void merge_group(const DecodeArgs& a, long long s, in
 }
 
 template <typename T, int D, int SH>
-__device__ void finish_splits(const DecodeArgs& a, const SplitPiece* sp, int nsp, int* s_flag) {
+__device__ __forceinline__ void finish_splits(const DecodeArgs& a, const SplitPiece* sp, int nsp, int* s_flag) {
   wait_stores();
   __syncthreads();
   if (threadIdx.x < nsp) {
@@ -251,20 +251,76 @@ __device__ void finish_splits(const DecodeArgs& a, const SplitPiece* sp, int nsp
     s_flag[threadIdx.x * 3 + 2] = q.np;
   }
   __syncthreads();
-  // Merge in one round of loads where the segment has at most 8 pieces (a
-  // decode batch): each thread requests (m_p, l_p, acc_p) of its output
-  // elements for all pieces at once and folds them into a running
-  // (maximum, denominator, sum). A longer segment (one sequence split over
-  // the grid) is merged four dims per thread, KW pieces per round of loads.
+  // A segment of at most 8 pieces (a decode batch's) is merged in one round
+  // of loads: each thread requests (m_p, l_p, acc_p) of its output elements
+  // for all pieces at once and folds them into a running (maximum,
+  // denominator, sum). A longer segment (one sequence split over the grid)
+  // is merged four dims per thread, kMergeWide pieces per round of loads.
   const int gc = a.chunk_heads;
   constexpr int E = 2;  // output elements per thread and pass
   constexpr int K = 8;  // pieces per batch of loads
   constexpr int DV = D / 4;  // four-dim groups per head (long segments)
+  // Short segments (at most K pieces), when a chunk's outputs fit one pass
+  // of two adjacent dims per thread: the pieces' (m, l) and partial pairs of
+  // every segment this workgroup merges are requested in one round of 8-byte
+  // loads (only the pieces there are), then folded as below.
+  bool short_done = false;
+  if (gc * D <= 2 * kThreads) {
+    bool merge[2];
+    int w0[2], np[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      merge[k] = k < nsp && s_flag[k * 3] && s_flag[k * 3 + 2] <= K;
+      w0[k] = s_flag[k * 3 + 1];
+      np[k] = s_flag[k * 3 + 2];
+    }
+    const int e2 = 2 * threadIdx.x;  // this thread's first output element of the chunk
+    const bool live = e2 < gc * D;
+    const int h = live ? e2 / D : 0;
+    const int d = live ? e2 - h * D : 0;
+    float mm[2][K], ll[2][K], a0[2][K], a1[2][K];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+#pragma unroll
+      for (int i = 0; i < K; ++i) {
+        if (merge[k] && i < np[k]) {
+          const size_t ent = ((size_t)(w0[k] + i + sp[k].s)) * SH + h;
+          get2(a.ws_ml + ent * 2, mm[k][i], ll[k][i]);
+          get2(a.ws_acc + ent * D + d, a0[k][i], a1[k][i]);
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      if (!merge[k]) continue;
+      float bm = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < K; ++i) bm = (i < np[k]) ? fmaxf(bm, mm[k][i]) : bm;
+      float x0 = 0.0f, x1 = 0.0f, ls = 0.0f;
+#pragma unroll
+      for (int i = 0; i < K; ++i) {
+        if (i < np[k]) {
+          const float f = __builtin_amdgcn_exp2f(mm[k][i] - bm);
+          x0 = fmaf(a0[k][i], f, x0);
+          x1 = fmaf(a1[k][i], f, x1);
+          ls = fmaf(ll[k][i], f, ls);
+        }
+      }
+      if (live) {
+        T* o = reinterpret_cast<T*>(a.out) + ((size_t)sp[k].b * a.n_heads + sp[k].h0) * D + e2;
+        store_out(o, x0 / ls);
+        store_out(o + 1, x1 / ls);
+      }
+      if (threadIdx.x == 0) __hip_atomic_store(a.ws_cnt + sp[k].s, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    short_done = true;
+  }
   for (int k = 0; k < nsp; ++k) {
     if (!s_flag[k * 3]) continue;
     const SplitPiece& q = sp[k];
     const int w0 = s_flag[k * 3 + 1];
     const int np = s_flag[k * 3 + 2];
+    if (short_done && np <= K) continue;  // merged above
     T* o = reinterpret_cast<T*>(a.out) + ((size_t)q.b * a.n_heads + q.h0) * D;
     if (np > K) {
       for (int v0 = 0; v0 < gc * DV; v0 += kThreads) {
@@ -339,6 +395,8 @@ struct ValuPiece {
   // Rows [r_begin, r_end) of segment (b, g, chunk). Writes the normalised
   // output when the piece is the whole segment, else the partial of `slot`.
   static constexpr bool kSpeculative = true;  // nothing but shared memory is touched before the gate
+  static constexpr bool kPair = false;
+  struct PieceRef {};
   static constexpr int kWgPerCu = 1;
   static __device__ __forceinline__ bool run(const DecodeArgs& a, Smem& sm, int b, int g, int chunk, int r_begin,
                              int r_end, int n, bool whole, long long slot, const int32_t* gate = nullptr) {
@@ -589,12 +647,18 @@ struct MfmaPiece {
   // The paged piece raises the device flag for table entries it reads
   // before its first loads, so it is never started ahead of its inputs.
   static constexpr bool kSpeculative = !PAGED;
+  // Static caches stream a workgroup's first two pieces as one (run_pair).
+  static constexpr bool kPair = !PAGED;
   // One workgroup per CU: measured faster than the two a CU could hold (fewer
   // pieces to merge, no second workgroup competing for issue slots and LDS).
   static constexpr int kWgPerCu = 1;
   static __device__ __forceinline__ bool run(const DecodeArgs& a, Smem& sm, int b, int kvg, int chunk,
                                              int r_begin, int r_end, int n, bool whole, long long slot,
                                              const int32_t* gate = nullptr) {
+    if constexpr (!PAGED) {
+      const PieceRef A{b, kvg, chunk, r_begin, r_end, n, whole, slot};
+      return run_pair(a, sm, A, A, false, gate);
+    }
     b = uniform(b);
     kvg = uniform(kvg);
     chunk = uniform(chunk);
@@ -816,6 +880,242 @@ struct MfmaPiece {
     return true;
   }
 
+
+  // One piece's fields.
+  struct PieceRef {
+    int b, kvg, chunk, r_begin, r_end, n;
+    bool whole;
+    long long slot;
+  };
+
+  // Static cache: a workgroup's pieces A and (hasB) B as one stream of tiles.
+  // Each wave takes its tiles of A, then its tiles of B, in one loop; one
+  // load sequence serves every tile (the piece's rows are chosen by uniform
+  // selects), so the ring keeps B's first tiles in flight while the last
+  // tiles of A are used and A is combined: the second piece starts without
+  // waiting for a first load. Same arithmetic, tile for tile, as one piece at
+  // a time. (The code is shaped for the compiler's wait counts: every round
+  // issues the same loads, and the rare branches, A's combine and the fused
+  // append's row write, only add memory operations.)
+  static __device__ __forceinline__ bool run_pair(const DecodeArgs& a, Smem& sm, const PieceRef& A,
+                                                  const PieceRef& Bp, bool hasB, const int32_t* gate) {
+    const int lane = threadIdx.x & 63;
+    const int wave = uniform(threadIdx.x >> 6);
+    const int g = lane >> 4;
+    const int j = lane & 15;
+    const int gc = a.chunk_heads;
+    const int group = a.n_heads / a.n_kv_heads;
+    const float scale_log2 = a.scale_log2;
+    const int stride = kWaves * TR;
+
+    const int a_b = uniform(A.b), a_kvg = uniform(A.kvg), a_rb = uniform(A.r_begin), a_re = uniform(A.r_end);
+    const int a_fresh = uniform(fused_row(a, a_re, A.n));
+    const int a_cache = a_fresh >= 0 ? a_fresh : a_re;  // rows read from the cache
+    const int a_h0 = a_kvg * group + uniform(A.chunk) * gc;
+    // B's fields (an empty piece when there is none: no rows, no tiles)
+    const int b_b = hasB ? uniform(Bp.b) : a_b, b_kvg = hasB ? uniform(Bp.kvg) : a_kvg;
+    const int b_rb = hasB ? uniform(Bp.r_begin) : 0, b_re = hasB ? uniform(Bp.r_end) : 0;
+    const int b_fresh = hasB ? uniform(fused_row(a, b_re, Bp.n)) : -1;
+    const int b_cache = b_fresh >= 0 ? b_fresh : b_re;
+    const int b_h0 = hasB ? b_kvg * group + uniform(Bp.chunk) * gc : a_h0;
+
+    // this wave's tiles: A's at a_rb + wave TR + t stride (t < TA), then B's
+    // at b_rb + wave TR + (t - TA) stride (t < total)
+    const int a_first = a_rb + wave * TR, b_first = b_rb + wave * TR;
+    const int TA = a_first < a_re ? (a_re - a_first + stride - 1) / stride : 0;
+    const int TB = b_first < b_re ? (b_re - b_first + stride - 1) / stride : 0;
+    const int total = TA + TB;
+
+    const int koff = j * (2 * D) + 16 * g;  // K row base + j, dims 8g.. of each 32-dim step
+    const int voff = lane * 16;             // V tile as contiguous 16-byte chunks
+    unsigned char* vs = sm.u.t.v[wave];
+
+    // Rows [base, base + TR) of tile t. Buffer resources span exactly the rows
+    // [0, cache) of the piece's (sequence, kv head); loads past them (the tail
+    // of the last tile, prefetches past the last tile) return zeros, and
+    // their scores are masked. The new row of a fused append lies outside
+    // them and is taken from k_new / v_new by the lanes that hold it.
+    auto load = [&](int t, bf16x8_t (&kr)[KS], u32x4_t (&vr)[VCH]) {
+      const bool inA = t < TA;
+      const int sb = inA ? a_b : b_b, skvg = inA ? a_kvg : b_kvg;
+      const int rows = inA ? a_cache : b_cache;
+      const int base = inA ? a_first + t * stride : b_first + (t - TA) * stride;
+      const int fresh = inA ? a_fresh : b_fresh;
+      const size_t row0 = ((size_t)sb * a.n_kv_heads + skvg) * (size_t)a.max_context;
+      const __amdgpu_buffer_rsrc_t kres =
+          buffer_rsrc(reinterpret_cast<const uint16_t*>(a.k) + row0 * D, rows * (2 * D));
+      const __amdgpu_buffer_rsrc_t vres =
+          buffer_rsrc(reinterpret_cast<const uint16_t*>(a.v) + row0 * D, rows * (2 * D));
+      const int kb = base * (2 * D) + koff;
+#pragma unroll
+      for (int k = 0; k < KS; ++k)
+        kr[k] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(kres, kb + 64 * k, 0, kStreamLoad));
+      const int vb = base * (2 * D) + voff;
+#pragma unroll
+      for (int i = 0; i < VCH; ++i) vr[i] = __builtin_amdgcn_raw_buffer_load_b128(vres, vb + 1024 * i, 0, kStreamLoad);
+      if (fresh >= base && fresh < base + TR) {  // this tile holds the new row
+        const size_t src = ((size_t)sb * a.n_kv_heads + skvg) * D;
+        const uint16_t* knew = reinterpret_cast<const uint16_t*>(a.k_new) + src;
+        const uint16_t* vnew = reinterpret_cast<const uint16_t*>(a.v_new) + src;
+        if (base + j == fresh) {
+#pragma unroll
+          for (int k = 0; k < KS; ++k) kr[k] = *reinterpret_cast<const bf16x8_t*>(knew + 32 * k + 8 * g);
+        }
+#pragma unroll
+        for (int i = 0; i < VCH; ++i) {
+          const int f = i * 64 + lane;
+          if (base + f / CPR == fresh) vr[i] = *reinterpret_cast<const u32x4_t*>(vnew + 8 * (f % CPR));
+        }
+      }
+    };
+
+    bf16x8_t qa[KS], qn[KS];  // the current piece's queries, and B's
+    f32x4_t o[NB];
+    float m, l;
+    auto reset = [&]() {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) o[nb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      m = -INFINITY;  // reference maximum of head column j (log2 units)
+      l = 0.0f;       // this lane's share of the softmax denominator of column j
+    };
+    reset();
+    // q as the B operand: column j is head h0 + j, zero past the chunk (a
+    // buffer resource over the chunk's gc heads returns zeros for those
+    // columns, so no select waits for the data)
+    auto load_q = [&](bf16x8_t (&q)[KS], int sb, int h0) {
+      const __amdgpu_buffer_rsrc_t qres =
+          buffer_rsrc(reinterpret_cast<const uint16_t*>(a.q) + ((size_t)sb * a.n_heads + h0) * D, gc * (2 * D));
+#pragma unroll
+      for (int k = 0; k < KS; ++k)
+        q[k] = __builtin_bit_cast(bf16x8_t,
+                                  __builtin_amdgcn_raw_buffer_load_b128(qres, j * (2 * D) + 64 * k + 16 * g, 0, 0));
+    };
+
+    // Tile t < total: raw scores q.k, the online softmax, p.v; the fused
+    // append's new row is written into the cache by chunk 0 from the
+    // registers that hold it (no piece reads the cache's copy of that row in
+    // this launch, so the write needs no ordering).
+    auto use = [&](int t, const bf16x8_t (&kr)[KS], const u32x4_t (&vr)[VCH]) {
+      const bool inA = t < TA;
+      const int base = inA ? a_first + t * stride : b_first + (t - TA) * stride;
+      const int r_end = inA ? a_re : b_re;
+      const int fresh = inA ? a_fresh : b_fresh;
+      // stage V row-major in LDS
+#pragma unroll
+      for (int i = 0; i < VCH; ++i) {
+        const int f = i * 64 + lane;
+        *reinterpret_cast<u32x4_t*>(vs + (f / CPR) * VSTRIDE + (f % CPR) * 16) = vr[i];
+      }
+      if (fresh >= base && fresh < base + TR && (inA ? A.chunk : Bp.chunk) == 0) {
+        const int sb = inA ? a_b : b_b, skvg = inA ? a_kvg : b_kvg;
+        const size_t row = ((size_t)sb * a.n_kv_heads + skvg) * (size_t)a.max_context + fresh;
+        uint16_t* kd = reinterpret_cast<uint16_t*>(const_cast<void*>(a.k)) + row * D;
+        uint16_t* vd = reinterpret_cast<uint16_t*>(const_cast<void*>(a.v)) + row * D;
+        if (base + j == fresh) {
+#pragma unroll
+          for (int k = 0; k < KS; ++k) *reinterpret_cast<bf16x8_t*>(kd + 32 * k + 8 * g) = kr[k];
+        }
+#pragma unroll
+        for (int i = 0; i < VCH; ++i) {
+          const int f = i * 64 + lane;
+          if (base + f / CPR == fresh) *reinterpret_cast<u32x4_t*>(vd + 8 * (f % CPR)) = vr[i];
+        }
+      }
+      // scores: s[u] = K[row base + 4g + u] . q[head column j]
+      f32x4_t s = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int k = 0; k < KS; ++k) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[k], qa[k], s, 0, 0, 0);
+      if (base + TR > r_end) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) s[u] = (base + 4 * g + u < r_end) ? s[u] : -INFINITY;
+      }
+      // online softmax with a lazily moved reference maximum: p and the bf16
+      // P operand keep full relative precision up to 2^kLazyMfma, so the
+      // reference is only moved (and o rescaled) when a score exceeds it by
+      // that much, which in practice happens only on a wave's first tile
+      const float cand = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])) * scale_log2;
+      if (__builtin_amdgcn_ballot_w64(cand > m + kLazyMfma)) {
+        float mt = fmaxf(cand, __shfl_xor(cand, 16));
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        const float mn = fmaxf(m, mt);
+        const float c = __builtin_amdgcn_exp2f(m - ((mn == -INFINITY) ? 0.0f : mn));
+        l *= c;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float ct = __shfl(c, 4 * g + u);  // factor of output row (head column) 4g + u
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) o[nb][u] *= ct;
+        }
+        m = mn;
+      }
+      const float nm = (m == -INFINITY) ? 0.0f : -m;
+      // P rounded to bf16 for the product; the denominator sums the same
+      // rounded weights, so the output is a convex combination of V rows
+      s16x4_t pa;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const __bf16 pb = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[u], scale_log2, nm));
+        pa[u] = __builtin_bit_cast(short, pb);
+        l += (float)pb;
+      }
+      // p.v: B operand = V[base + 4g + u][16 nb + j] by one transpose read
+      const unsigned char* vrow = vs + (4 * g + (j >> 2)) * VSTRIDE + 8 * (j & 3);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const s16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4_t*)(vrow + 32 * nb));
+        o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, o[nb], 0, 0, 0);
+      }
+    };
+    // A's end: combine it, then start B with its queries (every wave does
+    // this once, in order, before its first tile of B or after its last tile)
+    bool switched = false;
+    auto finish_a = [&]() {
+      combine(a, sm, o, m, l, a_b, a_h0, A.whole, A.slot);
+      reset();
+#pragma unroll
+      for (int k = 0; k < KS; ++k) qa[k] = qn[k];
+      switched = true;
+    };
+
+    // Software pipeline: a ring of NBUF register tiles, NBUF - 1 of them in
+    // flight while one is used. The first tile, then the queries of B and A
+    // (their latencies overlap), then the rest of the ring; the first use is
+    // taken out of the loop, so both queries are known to have arrived after
+    // it (loads complete in issue order; the loop then never waits for them).
+    bf16x8_t kbuf[NBUF][KS];
+    u32x4_t vbuf[NBUF][VCH];
+    load(0, kbuf[0], vbuf[0]);
+    load_q(qn, b_b, b_h0);
+    load_q(qa, a_b, a_h0);
+#pragma unroll
+    for (int i = 1; i < NBUF; ++i) load(i, kbuf[i], vbuf[i]);
+    if (gate) {  // the pieces were started before their inputs were confirmed
+      __syncthreads();
+      if (!*gate) return false;
+    }
+    if (total > 0) {
+      if (TA == 0) finish_a();
+      use(0, kbuf[0], vbuf[0]);
+    }
+    // tile t in buffer t mod NBUF; round t0 (= 1 mod NBUF) uses tiles t0 ..
+    // t0 + NBUF - 1 and loads tiles t0 + NBUF - 1 .. t0 + 2 NBUF - 2
+    for (int t0 = 1; t0 < total; t0 += NBUF) {
+#pragma unroll
+      for (int i = 0; i < NBUF; ++i) {
+        const int t = t0 + i;
+        load(t + NBUF - 1, kbuf[(1 + i + NBUF - 1) % NBUF], vbuf[(1 + i + NBUF - 1) % NBUF]);
+        if (t < total) {
+          if (t == TA) finish_a();
+          use(t, kbuf[(1 + i) % NBUF], vbuf[(1 + i) % NBUF]);
+        }
+      }
+    }
+    if (!switched) finish_a();
+    if (hasB) combine(a, sm, o, m, l, b_b, b_h0, Bp.whole, Bp.slot);
+    return true;
+  }
+
   // End of a piece: combine the waves' (o, m, l) and write the output (whole
   // segment) or the partial of `slot`. Every thread of the workgroup calls it.
   static __device__ __forceinline__ void combine(const DecodeArgs& a, Smem& sm, const f32x4_t (&o)[NB], float m,
@@ -937,6 +1237,8 @@ struct I8Piece {
   };
 
   static constexpr bool kSpeculative = true;  // nothing but shared memory is touched before the gate
+  static constexpr bool kPair = false;
+  struct PieceRef {};
   static __device__ __forceinline__ bool run(const DecodeArgs& a, Smem& sm, int b, int kvg, int chunk,
                                              int r_begin, int r_end, int n, bool whole, long long slot,
                                              const int32_t* gate = nullptr) {
@@ -1173,12 +1475,15 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(DecodeArgs a) {
   const bool key = plan_key(a.plan, a.n_wg, min_rows, B);
   const int entry_count = entry[0];  // requested with the header, whatever the key
   const int count = uniform(key ? entry_count : -1);  // pieces in this workgroup's cached entry
-  // The first cached piece's fields, requested now so that their latency
-  // overlaps the length scan below (read before it, the first loads of wave
-  // 0, and with them every wave's gate, waited for both in turn).
-  int first[kPieceInts];
+  // The first two cached pieces' fields, requested now so that their
+  // latency overlaps the length scan below (read before it, the first loads
+  // of wave 0, and with them every wave's gate, waited for both in turn).
+  int first[kPieceInts], second[kPieceInts];
 #pragma unroll
-  for (int i = 0; i < kPieceInts; ++i) first[i] = entry[1 + i];
+  for (int i = 0; i < kPieceInts; ++i) {
+    first[i] = entry[1 + i];
+    second[i] = entry[1 + kPieceInts + i];
+  }
   if (t < 64) {
     scan_lengths(a.valid_lens, a.cache_index, B, a.max_context, kSegRows, s_prefix, &s_umax, a.err_flag,
                  blockIdx.x == 0, min_rows, a.plan + KVC_PLAN_LENS, &st.gate);
@@ -1193,7 +1498,47 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(DecodeArgs a) {
   int nsplit = 0;
   if (speculate || (st.gate && count >= 1)) {
     bool planned = true;
-    for (int k = 0; k < count; ++k) {
+    int k0 = 0;
+    if constexpr (P::kPair) {
+      // the first two pieces as one stream (the second's first tiles are
+      // loaded while the first ends)
+      if (count >= 2) {
+        typename P::PieceRef pr[2];
+        int fs[2][kPieceInts];
+#pragma unroll
+        for (int i = 0; i < kPieceInts; ++i) {
+          fs[0][i] = uniform(first[i]);
+          fs[1][i] = uniform(second[i]);
+        }
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int hc = fs[q][1];
+          const long long s = (long long)fs[q][0] * HC + hc;
+          pr[q] = typename P::PieceRef{fs[q][0], hc / a.head_chunks, hc % a.head_chunks, fs[q][2], fs[q][3], fs[q][4],
+                                       fs[q][2] == 0 && fs[q][3] == fs[q][4], (long long)w + s};
+        }
+        if (!P::run_pair(a, sm, pr[0], pr[1], true, speculate ? &st.gate : nullptr)) {
+          planned = false;  // not this launch's plan: the gate's barrier published the prefix sums
+        } else {
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            if (!pr[q].whole && nsplit < 2) {
+              if (threadIdx.x == 0) {  // read after the barriers in finish_splits
+                split[nsplit].s = pr[q].slot - w;
+                split[nsplit].n = fs[q][4];
+                split[nsplit].b = fs[q][0];
+                split[nsplit].h0 = pr[q].kvg * (a.n_heads / a.n_kv_heads) + pr[q].chunk * a.chunk_heads;
+                split[nsplit].w0 = fs[q][5];
+                split[nsplit].np = fs[q][6];
+              }
+              ++nsplit;
+            }
+          }
+          k0 = 2;
+        }
+      }
+    }
+    for (int k = k0; planned && k < count; ++k) {
       const int32_t* pc = entry + 1 + k * kPieceInts;
       int f[kPieceInts];
 #pragma unroll
