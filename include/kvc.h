@@ -367,6 +367,31 @@ kvc_status kvc_set_workgroups(kvc_cache* cache, int32_t n);
  * largest accepted value. Host only. */
 kvc_status kvc_get_workgroups(const kvc_cache* cache, int32_t* n, int32_t* max_n);
 
+/* For callers that cannot allocate (code under HIP graph capture, serving
+ * loops and harnesses that forbid hipMalloc): kvc_decode_attn on a GQA layer
+ * the caller holds, without a kvc_cache. Nothing is allocated: the kernels'
+ * workspace (partials, arrival counters, the cached split of the work) is a
+ * 16 MiB static array on each device, held until the process ends.
+ *  desc:    the cache's shape (attn GQA, dtype bf16 or fp32; n_layers is not
+ *           used); validated as by kvc_alloc.
+ *  k_layer, v_layer: device pointers to one layer's K and V,
+ *           [B][H_kv][max_context][d_h] each, in the cache dtype.
+ *  q, out, valid_lens, cache_index, sm_scale: as for kvc_decode_attn, with
+ *           the same result bit for bit (same kernels, same default grid).
+ *  err_flag: device int32 the kernels set to 1 when a sequence's length is
+ *           out of range (that sequence's outputs are zeros); never cleared
+ *           by the library; may be NULL (the flag is then not reported).
+ * Host-checkable errors return a status and enqueue nothing: a bad
+ * descriptor or argument (KVC_ERR_INVALID_ARG / KVC_ERR_UNSUPPORTED as for
+ * kvc_alloc), an MLA or int8 shape, or a shape whose workspace exceeds the
+ * array (B * H > 65536, or (compute units + B * H) * 16 * (d_h + 2) * 4 bytes
+ * plus the split and counters above 16 MiB): KVC_ERR_UNSUPPORTED.
+ * Calls on one device share the array: calls that overlap in time on one
+ * device (concurrent streams) race and must not be issued. */
+kvc_status kvc_decode_attn_noalloc(const kvc_desc* desc, const void* k_layer, const void* v_layer, const void* q,
+                                   void* out, const int32_t* valid_lens, const int32_t* cache_index,
+                                   float sm_scale, int32_t* err_flag, void* stream);
+
 /* Synchronise `stream`, then report and clear the sticky device-range flag:
  * KVC_ERR_DEVICE_RANGE if any kernel since the last check skipped a
  * sequence, KVC_ERR_DEVICE if the stream reported an error, else KVC_OK. */

@@ -11,6 +11,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 
 #include "kvc_internal.h"
@@ -664,6 +665,103 @@ kvc_status kvc_get_workgroups(const kvc_cache* c, int32_t* n, int32_t* max_n) {
   *n = c->workgroups_forced;
   if (max_n) *max_n = c->max_workgroups;
   return KVC_OK;
+}
+
+}  // extern "C"
+
+// ---- decode attention for callers that cannot allocate --------------------
+//
+// kvc_decode_attn_noalloc runs the decode kernels of kvc_decode_attn with
+// their workspace in this static array (one copy on each device, zero when
+// the code object is loaded, held until the process ends) instead of the
+// one kvc_alloc makes. Layout, from the start: the cached split of the work
+// (its size fixed by the device's compute units), a flag word, the arrival
+// counters (a fixed region of kNoAllocCounters), then the (m, l) pairs and
+// the partial accumulators of the call's shape. The plan and the counters
+// therefore never overlap another shape's partials; the counters and the
+// plan's arrival count reset themselves at the end of every launch, and the
+// plan is keyed by grid, mode, batch, segments per sequence and lengths.
+// Calls that overlap on one device race on this memory.
+namespace {
+
+constexpr size_t kNoAllocBytes = 16u << 20;
+constexpr size_t kNoAllocCounters = 65536;  // (sequence, query head) pairs, at most
+__device__ __align__(256) static uint8_t scratch[kNoAllocBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t* g_scratch_ptr[kMaxDevices] = {};
+int g_scratch_cus[kMaxDevices] = {};
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// The device address of `scratch` on the current device (the host-side name
+// is not a device address) and its compute-unit count, looked up once per
+// device with that device current.
+kvc_status scratch_of_device(uint8_t** ptr, int* cus) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return KVC_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return KVC_ERR_DEVICE;
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+      return KVC_ERR_DEVICE;
+    g_scratch_ptr[dev] = (uint8_t*)p;
+    g_scratch_cus[dev] = n;
+  }
+  *ptr = g_scratch_ptr[dev];
+  *cus = g_scratch_cus[dev];
+  return KVC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvc_status kvc_decode_attn_noalloc(const kvc_desc* desc, const void* k_layer, const void* v_layer, const void* q,
+                                   void* out, const int32_t* valid_lens, const int32_t* cache_index,
+                                   float sm_scale, int32_t* err_flag, void* stream) {
+  kvc_status st = validate_desc(desc);
+  if (st != KVC_OK) return st;
+  if (desc->attn != KVC_ATTN_GQA || (desc->dtype != KVC_BF16 && desc->dtype != KVC_F32))
+    return KVC_ERR_UNSUPPORTED;
+  if (!k_layer || !v_layer || !q || !out || (!valid_lens && !cache_index)) return KVC_ERR_INVALID_ARG;
+  if (!(sm_scale > 0.0f) || sm_scale > 3.0e38f) return KVC_ERR_INVALID_ARG;
+  const uint64_t pairs = (uint64_t)desc->batch * desc->n_heads;
+  if (pairs > kNoAllocCounters) return KVC_ERR_UNSUPPORTED;
+  uint8_t* base = nullptr;
+  int cus = 0;
+  st = scratch_of_device(&base, &cus);
+  if (st != KVC_OK) return st;
+
+  // the launch as kvc_decode_attn makes it on a cache of this shape, with the
+  // default grid (one workgroup per compute unit for these dtypes)
+  kvc_cache c;
+  memset(&c, 0, sizeof(c));
+  c.d = *desc;
+  c.num_cus = cus;
+  c.elem = elem_size(desc->dtype);
+  c.row_elems = desc->head_dim;
+  c.max_workgroups = cus;
+  c.ws_entries = ((uint64_t)cus + pairs) * 16;
+  size_t off = 0;
+  c.ws_plan = (int32_t*)(base + off);
+  off += round256(((size_t)KVC_PLAN_HEAD + (size_t)cus * KVC_PLAN_INTS) * 4);
+  int32_t* own_flag = (int32_t*)(base + off);
+  off += 256;
+  c.ws_cnt = (int32_t*)(base + off);
+  off += round256(kNoAllocCounters * 4);
+  c.ws_ml = (float*)(base + off);
+  off += round256(c.ws_entries * 2 * sizeof(float));
+  c.ws_acc = (float*)(base + off);
+  off += round256(c.ws_entries * desc->head_dim * sizeof(float));
+  if (off > kNoAllocBytes) return KVC_ERR_UNSUPPORTED;
+  c.err_flag = err_flag ? err_flag : own_flag;
+  const hipError_t e = kvc_launch_gqa_decode(&c, k_layer, v_layer, q, out, valid_lens, cache_index, sm_scale,
+                                             (hipStream_t)stream);
+  return e == hipSuccess ? KVC_OK : KVC_ERR_DEVICE;
 }
 
 kvc_status kvc_check(kvc_cache* c, void* stream) {

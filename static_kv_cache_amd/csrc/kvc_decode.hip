@@ -1472,7 +1472,10 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(DecodeArgs a) {
   const int min_rows = a.k_new ? 1 : 0;
   const int HC = a.n_kv_heads * a.head_chunks;  // segments per sequence
   const int32_t* entry = plan_entry(a.plan);
-  const bool key = plan_key(a.plan, a.n_wg, min_rows, B);
+  // the plan's mode: append or not, and the segments per sequence (a cache's
+  // workspace serves one shape, a shared one may serve several)
+  const int plan_mode = min_rows + 2 * HC;
+  const bool key = plan_key(a.plan, a.n_wg, plan_mode, B);
   const int entry_count = entry[0];  // requested with the header, whatever the key
   const int count = uniform(key ? entry_count : -1);  // pieces in this workgroup's cached entry
   // The first two cached pieces' fields, requested now so that their
@@ -1613,7 +1616,7 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(DecodeArgs a) {
     });
     if (nsplit > 0) finish_splits<typename P::Elem, P::kD, P::kSlotHeads>(a, split, nsplit, s_flag);
   }
-  if (fresh) plan_publish(a.plan, st, recorded, s_prefix, B, kSegRows, a.n_wg, min_rows);
+  if (fresh) plan_publish(a.plan, st, recorded, s_prefix, B, kSegRows, a.n_wg, plan_mode);
 }
 
 template <class P, typename T, int D>

@@ -198,8 +198,9 @@ __device__ __forceinline__ void build_row_space(const int32_t* valid_lens, const
 // records its entry, and the last workgroup to finish publishes the header
 // (so no workgroup of that launch can see a header whose entries are not
 // written yet). Launches with an empty or out-of-range sequence never
-// publish. Layout (KVC_PLAN_* in kvc_internal.h): header [valid, grid, min
-// rows, batch, arrival count, 0, 0, 0], the lengths, then per workgroup a
+// publish. Layout (KVC_PLAN_* in kvc_internal.h): header [valid, grid, mode
+// (min rows + 2 x segments per sequence), batch, arrival count, 0, 0, 0],
+// the lengths, then per workgroup a
 // piece count (-1: more than kPlanPieces) and kPieceInts ints per piece
 // (b, hc, r_begin, r_end, n, w0, np; w0, np = the segment's first workgroup
 // and number of pieces, for pieces that are part of a segment).
@@ -212,13 +213,13 @@ struct PlanState {
   int32_t last;  // this workgroup publishes the new header
 };
 
-// Whether the header names this launch's grid, append mode and batch (the
-// lengths are compared by scan_lengths). Uniform: every wave reads it.
-__device__ __forceinline__ bool plan_key(const int32_t* plan, int n_wg, int min_rows, int B) {
+// Whether the header names this launch's grid, mode and batch (the lengths
+// are compared by scan_lengths). Uniform: every wave reads it.
+__device__ __forceinline__ bool plan_key(const int32_t* plan, int n_wg, int mode, int B) {
   // the four header words in one load, compared without short-circuit
   // branches (which made them four dependent loads at the kernel's start)
   const int4 h = *reinterpret_cast<const int4*>(plan);
-  return (h.x == 1) & (h.y == n_wg) & (h.z == min_rows) & (h.w == B);
+  return (h.x == 1) & (h.y == n_wg) & (h.z == mode) & (h.w == B);
 }
 
 // This workgroup's cached entry.
@@ -250,7 +251,7 @@ __device__ __forceinline__ void plan_record(int32_t* plan, int& recorded, int b,
 // launch publishes the header for the lengths in s_prefix (u_b = n_b +
 // seg_rows per non-empty sequence).
 __device__ __forceinline__ void plan_publish(int32_t* plan, PlanState& st, int recorded, const int32_t* s_prefix,
-                                             int B, int seg_rows, int n_wg, int min_rows) {
+                                             int B, int seg_rows, int n_wg, int mode) {
   const int t = threadIdx.x;
   if (t == 0) {
     plan[KVC_PLAN_HEAD + (size_t)blockIdx.x * KVC_PLAN_INTS] = recorded;
@@ -268,7 +269,7 @@ __device__ __forceinline__ void plan_publish(int32_t* plan, PlanState& st, int r
   const int usable = __syncthreads_and(all ? 1 : 0);
   if (t == 0) {
     plan[1] = n_wg;
-    plan[2] = min_rows;
+    plan[2] = mode;
     plan[3] = B;
     plan[4] = 0;
     plan[0] = usable ? 1 : 0;

@@ -54,6 +54,7 @@ _SIGS = {
     "kvc_prefill_fill": [_p, _i32, _p, _p, _i32, _i32, _p],
     "kvc_append": [_p, _i32, _p, _p, _p, _i32, _p],
     "kvc_decode_attn": [_p, _i32, _p, _p, _p, _p, ctypes.c_float, _p],
+    "kvc_decode_attn_noalloc": [ctypes.POINTER(Desc), _p, _p, _p, _p, _p, _p, ctypes.c_float, _p, _p],
     "kvc_mla_decode": [_p, _i32, _p, _p, _p, _p, _p, _p, _p, ctypes.c_float, _p],
     "kvc_append_decode_attn": [_p, _i32, _p, _p, _p, _p, _p, ctypes.c_float, _p],
     "kvc_prefill_attn": [_p, _i32, _p, _p, _p, _p, _i32, _i32, ctypes.c_float, _p],
@@ -409,6 +410,40 @@ class Cache:
             self.free()
         except Exception:
             pass
+
+
+def decode_attn_noalloc(desc, k_layer, v_layer, q, out, valid_lens=None, cache_index=None, sm_scale=None,
+                        err_flag=None):
+    """kvc_decode_attn_noalloc: decode attention over one GQA layer the caller
+    holds (k_layer, v_layer [B][H_kv][max_context][d_h], bf16 or fp32), with
+    the library's static workspace (no allocation). err_flag: optional device
+    int32 tensor of one element that the kernels set on an out-of-range
+    length."""
+    torch = _torch()
+    dtype = {KVC_F32: "f32", KVC_BF16: "bf16"}.get(desc.dtype)
+    if dtype is None:
+        raise ValueError("decode_attn_noalloc takes bf16 or fp32 GQA shapes")
+    want = torch_dtype(dtype)
+    dev = q.device
+
+    def ptr(t, shape, dt, name):
+        if t is None:
+            return None
+        if t.device != dev or t.dtype != dt or tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} must be {dt} of shape {tuple(shape)} on {dev}")
+        if not t.is_contiguous() or t.data_ptr() % 16 != 0:
+            raise ValueError(f"{name} must be contiguous and 16-byte aligned")
+        return ctypes.c_void_p(t.data_ptr())
+
+    kv = (desc.batch, desc.n_kv_heads, desc.max_context, desc.head_dim)
+    qo = (desc.batch, desc.n_heads, desc.head_dim)
+    if sm_scale is None:
+        raise ValueError("sm_scale is required")
+    _call("kvc_decode_attn_noalloc", ctypes.byref(desc), ptr(k_layer, kv, want, "k_layer"),
+          ptr(v_layer, kv, want, "v_layer"), ptr(q, qo, want, "q"), ptr(out, qo, want, "out"),
+          ptr(valid_lens, (desc.batch,), torch.int32, "valid_lens"),
+          ptr(cache_index, (desc.batch,), torch.int32, "cache_index"), float(sm_scale),
+          ptr(err_flag, (1,), torch.int32, "err_flag"), _stream(dev))
 
 
 def paged_cache_bytes(desc, block_size, num_blocks):

@@ -174,3 +174,22 @@ def test_prefix_calls_reject_null_handles(lib):
     assert lib.kvc_prefix_bytes(None, lens, ctypes.byref(n)) == kvc.KVC_ERR_INVALID_ARG
     assert lib.kvc_save_prefix(None, lens, z, 4096, None) == kvc.KVC_ERR_INVALID_ARG
     assert lib.kvc_load_prefix(None, z, 4096, lens, lens, None) == kvc.KVC_ERR_INVALID_ARG
+
+
+def test_noalloc_decode_rejects_before_any_device_call(lib):
+    """kvc_decode_attn_noalloc checks its descriptor and arguments on the host
+    first: bad ones return a status without touching the device."""
+    fn = lib.kvc_decode_attn_noalloc
+    p = ctypes.c_void_p(16)  # never dereferenced: every call below is rejected first
+    good = kvc.gqa_desc(1, 2, 8, 2, 128, 64, "bf16")
+    assert fn(None, p, p, p, p, p, p, 0.125, None, None) == kvc.KVC_ERR_INVALID_ARG
+    assert fn(ctypes.byref(good), None, p, p, p, p, p, 0.125, None, None) == kvc.KVC_ERR_INVALID_ARG
+    assert fn(ctypes.byref(good), p, p, p, None, p, p, 0.125, None, None) == kvc.KVC_ERR_INVALID_ARG
+    assert fn(ctypes.byref(good), p, p, p, p, None, None, 0.125, None, None) == kvc.KVC_ERR_INVALID_ARG
+    assert fn(ctypes.byref(good), p, p, p, p, p, p, 0.0, None, None) == kvc.KVC_ERR_INVALID_ARG
+    i8 = kvc.gqa_desc(1, 2, 8, 2, 128, 64, "i8")
+    assert fn(ctypes.byref(i8), p, p, p, p, p, p, 0.125, None, None) == kvc.KVC_ERR_UNSUPPORTED
+    mla = kvc.mla_desc(1, 2, 16, 64)
+    assert fn(ctypes.byref(mla), p, p, p, p, p, p, 0.125, None, None) == kvc.KVC_ERR_UNSUPPORTED
+    wide = kvc.gqa_desc(1, 2048, 64, 8, 128, 64, "bf16")  # 131,072 (sequence, head) pairs
+    assert fn(ctypes.byref(wide), p, p, p, p, p, p, 0.125, None, None) == kvc.KVC_ERR_UNSUPPORTED
