@@ -64,7 +64,12 @@ static_assert(kQT == 16, "a wave's q.k dims are 32 kQS + 16");
 constexpr int kVec = kTok * kRowBytes / 16 / kThreads;  // staged 16-byte vectors per thread per tile
 constexpr int kRowVecs = kRowBytes / 16;     // 72
 constexpr int kSlotHeads = 16;               // partial entries per workspace slot
-constexpr int kSegRowsMla = 160;             // start-up rows of a segment (see kvc_device.h)
+// Start-up rows of a segment (see kvc_device.h): none. A segment's first
+// piece costs little beyond its rows here, and with 8 workgroups per segment
+// (B = 32, 4096 rows) any allowance lands on the same eighth of the grid
+// (the workgroups of one XCD): 160 rows made them finish 9 us before the
+// rest (latent attention 37.6 -> 36.3 us without).
+constexpr int kSegRowsMla = 0;
 constexpr float kLazyMfma = 64.0f;           // log2 headroom before the reference maximum moves
 static_assert(kTok * kRowBytes % (16 * kThreads) == 0, "tile must split evenly over the threads");
 static_assert(kSegRowsMla <= kMaxSegRows, "row space must stay below 2^31");
