@@ -254,23 +254,32 @@ __device__ __forceinline__ void mla_piece(const MlaArgs& a, unsigned char* tiles
     use_tile(tile1, t0 + kTok);
   }
 
-  // denominators of the head columns, then the partial o~ / l, m and l
+  // denominators of the head columns, then the partial o~ / l (bf16, put
+  // together in LDS as [head][column] and stored 16 bytes per lane), m and
+  // l. The stores write through to memory (sc1), so the launch's end has no
+  // dirty partials to write back from the L2s: with plain stores the next
+  // launch started up to 2 us later on six of the eight XCDs.
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
+  __syncthreads();  // every wave is done with the tiles
+  uint16_t* const po = reinterpret_cast<uint16_t*>(tiles);  // [16][512] bf16 (16 KB)
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int hr = 4 * g + t;
-    const float lr = __shfl(l, hr);
-    if (hr < gc) {
-      const float inv = 1.0f / lr;  // lr >= 1: the piece has a live row
-      uint16_t* dst = a.part + ((size_t)slot * kSlotHeads + hr) * kDc + kCols * wave + j;
+    const float inv = 1.0f / __shfl(l, hr);  // l >= 1: the piece has a live row
 #pragma unroll
-      for (int nb = 0; nb < kNB; ++nb) dst[16 * nb] = bf16_rne(o[nb][t] * inv);
-    }
+    for (int nb = 0; nb < kNB; ++nb) po[hr * kDc + kCols * wave + 16 * nb + j] = bf16_rne(o[nb][t] * inv);
+  }
+  __syncthreads();
+  const __amdgpu_buffer_rsrc_t pres = buffer_rsrc(a.part + (size_t)slot * kSlotHeads * kDc, gc * kDc * 2);
+#pragma unroll
+  for (int i = 0; i < kSlotHeads * kDc / 8 / kThreads; ++i) {
+    const int v = (int)threadIdx.x + kThreads * i;  // 16-byte vector v: head v / 64, columns 8 (v % 64) ..
+    __builtin_amdgcn_raw_buffer_store_b128(reinterpret_cast<const u32x4_t*>(po)[v], pres, 16 * v, 0, kWriteThrough);
   }
   if (wave == 0 && g == 0 && j < gc) {
-    a.ml[((size_t)slot * kSlotHeads + j) * 2] = m;
-    a.ml[((size_t)slot * kSlotHeads + j) * 2 + 1] = l;
+    put(a.ml + ((size_t)slot * kSlotHeads + j) * 2, m);
+    put(a.ml + ((size_t)slot * kSlotHeads + j) * 2 + 1, l);
   }
   __syncthreads();  // the tiles are reused by the next piece
 }
