@@ -255,10 +255,9 @@ __device__ __forceinline__ void mla_piece(const MlaArgs& a, unsigned char* tiles
   }
 
   // denominators of the head columns, then the partial o~ / l (bf16, put
-  // together in LDS as [head][column] and stored 16 bytes per lane), m and
-  // l. The stores write through to memory (sc1), so the launch's end has no
-  // dirty partials to write back from the L2s: with plain stores the next
-  // launch started up to 2 us later on six of the eight XCDs.
+  // together in LDS as [head][column] and stored 16 bytes per lane, written
+  // through to memory), m and l. Against one 2-byte store per element this
+  // took the latent attention from 35.0 to 34.1 us (B = 32, 4096 rows).
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
   __syncthreads();  // every wave is done with the tiles
