@@ -18,8 +18,11 @@ constexpr int kBufWord3 = 0x00020000;  // raw buffer resource word 3 (32-bit dat
 // the Infinity Cache (Llama-3-shaped layer: 36.0 -> 33.9 us; sc0 made no
 // difference and sc1 was slower).
 constexpr int kStreamLoad = 2;
-// Cache policy "sc1" of a raw buffer store: written through to memory.
+// Cache policy "sc1" of a raw buffer store (written through to memory) and
+// of a raw buffer load (coherent at device scope, as the relaxed agent-scope
+// accesses below: reads partials stored by workgroups on other XCDs).
 constexpr int kWriteThrough = 16;
+constexpr int kCoherentLoad = 16;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
