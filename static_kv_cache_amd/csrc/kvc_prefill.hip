@@ -16,7 +16,7 @@
 //    wave w takes head hpw0 + w % hpw and 16 positions. The K/V tiles of the
 //    kv head are therefore shared by all heads of the group the workgroup
 //    holds.
-//  - Keys go in tiles of 64 rows (32 for d_h = 256), K and V each copied
+//  - Keys go in tiles of 32 rows, K and V each copied
 //    from memory straight into LDS by the waves' buffer loads (no registers,
 //    no LDS write instructions), into two buffers used in turn: the next
 //    tile's copy is issued right after the barrier that opens the current
@@ -45,7 +45,7 @@ using namespace kvcd;
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kLazy = 64.0f;            // log2 headroom before the reference maximum moves
-constexpr int kQueryGroups = 1;           // query groups of 16 per wave (1, 2, 3 measured alike; 4 slower)
+constexpr int kQueryGroups = 1;           // query groups of 16 per wave (2 measured within noise of 1)
 
 struct PrefillArgs {
   const uint16_t* k;      // layer keys [B][H_kv][S][D]
@@ -62,7 +62,9 @@ template <int D>
 struct Prefill {
   static constexpr int KS = D / 32;                 // q.k steps of 32 dims
   static constexpr int NB = D / 16;                 // output column blocks
-  static constexpr int TK = D <= 128 ? 64 : 32;     // keys per tile
+  // keys per tile: 32 (a 64-key tile doubles the LDS per workgroup and
+  // halves the workgroups a CU holds: 188 vs 215 us at a 4096-token prompt)
+  static constexpr int TK = 32;
   static constexpr int NKB = TK / 16;               // 16-key blocks per tile
   static constexpr int ROW = 2 * D;                 // bytes per staged row
   static constexpr int CPR = ROW / 16;              // 16-byte chunks per row
@@ -127,15 +129,18 @@ __global__ __launch_bounds__(kThreads) void prefill_attn_kernel(PrefillArgs a) {
             bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(qres, (p0 + 16 * qg + j) * P::ROW + 64 * k + 16 * g, 0, 0));
   }
 
-  f32x4_t o[QG][P::NB];
-  float m[QG], l[QG];
+  // o, and in lsum the denominators: the product of P with a block of ones,
+  // so lsum[qg][w] is the sum of the bf16 weights of output row (query) 4g + w
+  f32x4_t o[QG][P::NB], lsum[QG];
+  float m[QG];
 #pragma unroll
   for (int qg = 0; qg < QG; ++qg) {
 #pragma unroll
     for (int nb = 0; nb < P::NB; ++nb) o[qg][nb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    lsum[qg] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     m[qg] = -INFINITY;
-    l[qg] = 0.0f;
   }
+  const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
   const float scale_log2 = a.scale_log2;
 
   // Copy of the tile at key k0 into buffer u: wave w's copy i fills bytes
@@ -195,27 +200,26 @@ __global__ __launch_bounds__(kThreads) void prefill_attn_kernel(PrefillArgs a) {
         mt = fmaxf(mt, __shfl_xor(mt, 32));
         const float mn = fmaxf(m[qg], mt);
         const float c = __builtin_amdgcn_exp2f(m[qg] - ((mn == -INFINITY) ? 0.0f : mn));
-        l[qg] *= c;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           const float cw = __shfl(c, 4 * g + w);  // factor of output row (query) 4g + w
 #pragma unroll
           for (int nb = 0; nb < P::NB; ++nb) o[qg][nb][w] *= cw;
+          lsum[qg][w] *= cw;
         }
         m[qg] = mn;
       }
       const float nm = (m[qg] == -INFINITY) ? 0.0f : -m[qg];
       // P as the A operand of 32-key products: lane (g, j) takes keys
       // 4g .. 4g + 3 of both blocks of a pair (the order of the transposed V
-      // reads); the denominator sums the bf16 weights that enter the product
+      // reads); the denominator sums the same bf16 weights, on the matrix cores
 #pragma unroll
-      for (int pp = 0; pp < P::NKB / 2; ++pp)
+      for (int pp = 0; pp < P::NKB / 2; ++pp) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const __bf16 pb = (__bf16)__builtin_amdgcn_exp2f(fmaf(sc[2 * pp + (e >> 2)][e & 3], scale_log2, nm));
-          l[qg] += (float)pb;
-          pa[qg][pp][e] = pb;
-        }
+        for (int e = 0; e < 8; ++e)
+          pa[qg][pp][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sc[2 * pp + (e >> 2)][e & 3], scale_log2, nm));
+        lsum[qg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[qg][pp], ones, lsum[qg], 0, 0, 0);
+      }
     }
     // p.v: B operand = V[k0 + 16 kb + 4g + w][16 nb + j] of both blocks of a
     // pair by one transposed read each, shared by the query groups
@@ -257,13 +261,10 @@ __global__ __launch_bounds__(kThreads) void prefill_attn_kernel(PrefillArgs a) {
   // normalise and write: lane (g, j) holds output rows (queries) 4g + w, columns 16 nb + j
 #pragma unroll
   for (int qg = 0; qg < QG; ++qg) {
-    float lq = l[qg];
-    lq += __shfl_xor(lq, 16);
-    lq += __shfl_xor(lq, 32);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const int qi = p0 + 16 * qg + 4 * g + w;
-      const float lr = __shfl(lq, 4 * g + w);
+      const float lr = lsum[qg][w];
       if (qi < a.t) {
         uint16_t* dst = a.out + (((size_t)b * a.n_heads + h) * a.t + qi) * D + j;
         const float inv = 1.0f / lr;  // lr >= 1: the query attends at least its own key
