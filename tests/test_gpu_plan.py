@@ -110,3 +110,34 @@ def test_overflowing_plan_entries(workgroups):
                       f"workgroups {workgroups}")
             seen[key] = out
     cache.free()
+
+
+@pytest.mark.parametrize("D,lens", [
+    (32, (512, 1, 300, 0, 512, 17, 200, 511)),    # every segment short: each goes whole to one workgroup
+    (32, (513, 1, 300, 0, 512, 17, 200, 511)),    # one segment one row longer: the split over the grid
+    (128, (256, 255, 3, 0, 128, 256, 1, 100)),    # 128 KB rows limit at d_h = 128: whole
+    (128, (257, 255, 3, 0, 128, 256, 1, 100)),    # one row over it: split
+])
+def test_short_segments_whole_and_split(D, lens):
+    """On the default grid, segments of at most 512 rows and 128 KB of rows are each taken whole by
+    one workgroup; one row more switches to the split over the grid. Both sides of the boundary, in
+    turn on one cache (the cached split follows the lengths), with ragged and empty sequences, match
+    the oracle, and a forced grid (always split) matches it too."""
+    dev = device()
+    B, H, Hkv, S = 8, 8, 4, 520
+    cache, ref, q, _ = setup(dev, B, H, Hkv, D, S, 23)
+    qd = kvc.to_device(q, dev)
+    scale = 1.0 / np.sqrt(D)
+    want = oatt.decode_attention(q, ref.keys(0), ref.values(0), list(lens), scale)
+    other = tuple(min(n + 1, S) if n else 0 for n in lens)
+    want_other = oatt.decode_attention(q, ref.keys(0), ref.values(0), list(other), scale)
+    for wg, seq in ((0, (lens, other, lens)), (48, (lens,))):
+        cache.set_workgroups(wg)
+        for cur in seq:
+            say(f"short segments: d_h {D} workgroups {wg} lengths {cur}")
+            out = torch.empty((B, H, D), dtype=torch.bfloat16, device=dev)
+            cache.decode_attn(0, qd, out, valid_lens=kvc.to_device(np.array(cur, dtype=np.int32), dev),
+                              sm_scale=scale)
+            cache.check()
+            tol_check(to_f64(out), want if cur == lens else want_other, "bf16", f"wg {wg} lens {cur}")
+    cache.free()
