@@ -69,13 +69,22 @@ def us_fields(prefix, st):
             f"{prefix}_us_p90": round(st["p90"], 3)}
 
 
-def burst_stats(torch, fn, L, bursts, warmup):
+def burst_stats(torch, fn, L, bursts, warmup, warm_s=0.2):
     """Per-launch time of fn(layer): `bursts` bursts of L back-to-back launches
     (layers 0..L-1), one HIP event pair around each burst on the launch
-    stream; one sample per burst (burst time / L). Returns pct()."""
-    for _ in range(warmup):
+    stream; one sample per burst (burst time / L). Returns pct().
+    Before them, `warmup` untimed bursts and at least `warm_s` seconds of
+    launches: after the GPU has idled (a leg's set-up copies its data from
+    the host), its first tens of ms of back-to-back work run slower (up to
+    20 % for the prefill and ~3 % for the latent attention)."""
+    import time
+    t_end = time.perf_counter() + warm_s
+    n = 0
+    while n < warmup or time.perf_counter() < t_end:
         for layer in range(L):
             fn(layer)
+        torch.cuda.synchronize()
+        n += 1
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(bursts)]
     torch.cuda.synchronize()
     for e0, e1 in evs:
@@ -275,7 +284,7 @@ def bench_mla(torch, steps, warmup, workgroups=0):
                **us_fields("latent_attn", lat), kv_gbs=round(gbs, 2),
                hbm_peak_frac=round(gbs / HBM_PEAK_GBS, 4),
                **us_fields("step", stp), layer_steps_per_s=round(1.0 / (step_ms * 1e-3), 1),
-               timing=f"median (p10, p90) over {steps} bursts of {L} back-to-back launches, HIP events",
+               timing=f"median (p10, p90) over {steps} bursts of {L} back-to-back launches, HIP events, after at least 0.2 s of warm-up launches",
                step="append + absorb + latent attention (split, merge) + up-projection")
     log(f"bench: mla latent attention {lat_ms * 1e3:.2f} us ({gbs:.1f} GB/s), step {step_ms * 1e3:.2f} us")
     wl.cache.free()
@@ -350,7 +359,7 @@ def bench_i8(torch, steps, warmup, bf16_decode_us, workgroups=0):
                **us_fields("step", stp), layer_steps_per_s=round(1.0 / (step_ms * 1e-3), 1),
                decode_steps_per_s=round(1.0 / (step_ms * 1e-3 * L), 2),
                step_two_launches_us=round(two_ms * 1e3, 3),
-               timing=f"median (p10, p90) over {steps} bursts of {L} back-to-back launches, HIP events",
+               timing=f"median (p10, p90) over {steps} bursts of {L} back-to-back launches, HIP events, after at least 0.2 s of warm-up launches",
                step="kvc_append_decode_attn (quantise, append and attend the new rows in one launch), per layer")
     log(f"bench: i8 decode {dec_ms * 1e3:.2f} us ({gbs:.1f} GB/s of codes and scales), "
         f"step {step_ms * 1e3:.2f} us (two launches {two_ms * 1e3:.2f} us); bf16 decode {bf16_decode_us:.2f} us")
@@ -429,7 +438,7 @@ def bench_paged(torch, steps, warmup, bf16_decode_us):
                vs_static_decode=round(bf16_decode_us / (dec_ms * 1e3), 3),
                **us_fields("step", stp), layer_steps_per_s=round(1.0 / (step_ms * 1e-3), 1),
                step_two_launches_us=round(two_ms * 1e3, 3),
-               timing=f"median (p10, p90) over {steps} bursts of {L} back-to-back launches, HIP events",
+               timing=f"median (p10, p90) over {steps} bursts of {L} back-to-back launches, HIP events, after at least 0.2 s of warm-up launches",
                step="kvc_paged_append_decode_attn (append through the table + decode, one launch), per layer")
     log(f"bench: paged decode {dec_ms * 1e3:.2f} us ({gbs:.1f} GB/s), step {step_ms * 1e3:.2f} us "
         f"(two launches {two_ms * 1e3:.2f} us); static decode {bf16_decode_us:.2f} us")
@@ -487,7 +496,7 @@ def bench_longctx(torch, steps, warmup, workgroups=0):
                 valid_len=sum_valid, layers_allocated=Lalloc, layers_rotated=L, kv_bytes_per_layer=kv_bytes,
                 **us_fields("decode", dec), kv_gbs=round(gbs, 2), hbm_peak_frac=round(gbs / HBM_PEAK_GBS, 4),
                 **us_fields("step", stp), layer_steps_per_s=round(1.0 / (step_ms * 1e-3), 1),
-                timing=f"median (p10, p90) over {steps} bursts of {L} back-to-back launches, HIP events",
+                timing=f"median (p10, p90) over {steps} bursts of {L} back-to-back launches, HIP events, after at least 0.2 s of warm-up launches",
                 step="kvc_append_decode_attn (append + decode attention, one launch), per layer")
 
 
@@ -512,15 +521,7 @@ def bench_prefill(torch, steps, warmup):
     def fn(layer):
         cache.prefill_attn(layer, q, k, v, out, 0, scale)
 
-    # back-to-back matrix-core work runs slower for its first tens of ms (the
-    # first bursts of a run read up to 20 % longer): warm up for 0.3 s first
-    import time
-    t_end = time.perf_counter() + 0.3
-    while time.perf_counter() < t_end:
-        for layer in range(L):
-            fn(layer)
-        torch.cuda.synchronize()
-    st = burst_stats(torch, fn, L, steps, warmup)
+    st = burst_stats(torch, fn, L, steps, warmup, warm_s=0.3)
     ms = st["median"] * 1e-3
     cache.check()
     cache.free()
@@ -530,7 +531,7 @@ def bench_prefill(torch, steps, warmup):
     return dict(workload="llama3_8b_prompt4096_bf16", batch=B, n_heads=H, n_kv_heads=Hkv, head_dim=D, tokens=T,
                 **us_fields("layer", st), flops_per_layer=flops, tflops=round(tf, 2),
                 timing=f"median (p10, p90) over {steps} bursts of {L} back-to-back launches, HIP events, "
-                       "after 0.3 s of warm-up launches",
+                       "after at least 0.3 s of warm-up launches",
                 mfma_peak_frac=round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
                 ttft_attention_ms_32_layers=round(ms * 32, 3),
                 step="kvc_prefill_attn: write the prompt rows into the cache + causal attention, per layer")
@@ -824,7 +825,7 @@ def main():
                 alg_bytes_per_launch=wl.fused_alg_bytes, **us_fields("launch", fused),
                 mean_launch_us=round(fused["mean"], 3),
                 timing=(f"HIP events on the launch stream: median (p10, p90) over {args.steps} bursts of {L} "
-                        f"back-to-back launches over the 32 layers"),
+                        f"back-to-back launches over the 32 layers, after at least 0.2 s of warm-up launches"),
                 event_pair_us=round(pair_ms * 1e3, 3),
                 **us_fields("decode_only", dec),
                 decode_only_achieved=round(wl.decode_alg_bytes / (decode_ms * 1e-3) / 1e9, 2),
