@@ -20,7 +20,9 @@
 //  - A piece is streamed ONCE and applied to all query heads of its head
 //    chunk. bf16 caches (MfmaPiece): each wave takes 16-row tiles in turn;
 //    q.k is one v_mfma_f32_16x16x32_bf16 per 32 dims with the 16 K rows as
-//    the A operand (loaded straight from HBM as 16-byte vectors) and the
+//    the A operand (static caches: loaded from HBM as whole 1 KB blocks,
+//    staged in LDS and read back in the operand's layout; block-table
+//    caches: loaded in that layout) and the
 //    chunk's query heads, zero-padded to 16, as the B operand; the score
 //    tile that comes out is exactly the A operand of p.v
 //    (v_mfma_f32_16x16x16_bf16, K = the 16 rows), and V reaches its B
@@ -660,6 +662,12 @@ struct MfmaPiece {
   static constexpr int CPR = D / 8;            // 16-byte chunks per row
   static constexpr int VCH = TR * CPR / 64;    // V chunks per lane per tile
   static constexpr int VSTRIDE = 2 * D + 32;   // bytes per staged V row (skew spreads LDS banks)
+  // K staged through LDS (static caches with rows wider than 64 bytes; see
+  // stage_k), and the bytes per staged K row: the 16-byte skew puts the 16
+  // rows an A-operand read touches (one 16-byte column, lanes of one g) on 16
+  // different bank quads
+  static constexpr bool kStageK = !PAGED && D > 32;
+  static constexpr int KSTRIDE = 2 * D + 16;
   static constexpr int NBUF = D <= 64 ? 3 : 2; // register tiles in the ring (register budget)
   static_assert(D % 32 == 0 && VCH >= 1 && TR * CPR % 64 == 0, "head_dim must be 32..256");
   static constexpr int kTable = PAGED ? KVC_MAX_TABLE : 1;
@@ -668,6 +676,7 @@ struct MfmaPiece {
     union {
       struct {
         unsigned char v[kWaves][TR * VSTRIDE];  // per-wave V staging (tile loop)
+        unsigned char k[kWaves][kStageK ? TR * KSTRIDE : 16];  // per-wave K staging (tile loop)
         int32_t blk[kTable];                    // block-table caches: block offsets of the piece's rows
       } t;
       struct {
@@ -686,6 +695,37 @@ struct MfmaPiece {
   // One workgroup per CU: measured faster than the two a CU could hold (fewer
   // pieces to merge, no second workgroup competing for issue slots and LDS).
   static constexpr int kWgPerCu = 1;
+
+  // With kStageK, K tiles are loaded like V tiles, as contiguous 16-byte
+  // chunks (chunk i of lane l is chunk f % CPR of row f / CPR, f = 64 i + l),
+  // so every load instruction reads 1 KB of whole cache lines; a load in the
+  // A-operand layout reads 64 bytes of each of 16 rows, which at rows wider
+  // than 64 bytes sends twice the requests (Llama-3 layer 32.6 -> 31.6 us,
+  // int8 23.6 -> 22.5 us). At d_h = 32 that layout is itself one contiguous
+  // 1 KB block, and the staging would only add latency (a 12-layer step at
+  // d_h = 32: 86 -> 91 us). The tile is staged in the wave's LDS area ...
+  static __device__ __forceinline__ void stage_k(unsigned char* ks, const bf16x8_t (&kr)[KS]) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < KS; ++i) {
+      const int f = i * 64 + lane;
+      *reinterpret_cast<bf16x8_t*>(ks + (f / CPR) * KSTRIDE + (f % CPR) * 16) = kr[i];
+    }
+  }
+  // ... and read back as the A operand of q.k: lane (g, j) takes row j, dims
+  // [32 k + 8 g, 32 k + 8 g + 8) in step k, so s[t] = K[row 4g + t] . q[head
+  // column j].
+  static __device__ __forceinline__ f32x4_t scores(const unsigned char* ks, const bf16x8_t (&q)[KS]) {
+    const int lane = threadIdx.x & 63;
+    const unsigned char* row = ks + (lane & 15) * KSTRIDE + 16 * (lane >> 4);
+    bf16x8_t av[KS];
+#pragma unroll
+    for (int k = 0; k < KS; ++k) av[k] = *reinterpret_cast<const bf16x8_t*>(row + 64 * k);
+    f32x4_t s = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int k = 0; k < KS; ++k) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[k], q[k], s, 0, 0, 0);
+    return s;
+  }
   static __device__ __forceinline__ bool run(const DecodeArgs& a, Smem& sm, int b, int kvg, int chunk,
                                              int r_begin, int r_end, int n, bool whole, long long slot,
                                              const int32_t* gate = nullptr) {
@@ -732,8 +772,11 @@ struct MfmaPiece {
     const int r_cache = fresh >= 0 ? fresh : r_end;  // rows read from the cache
     const __amdgpu_buffer_rsrc_t kres = PAGED ? buffer_rsrc(a.k, a.pool_bytes) : buffer_rsrc(kbase, r_cache * (2 * D));
     const __amdgpu_buffer_rsrc_t vres = PAGED ? buffer_rsrc(a.v, a.pool_bytes) : buffer_rsrc(vbase, r_cache * (2 * D));
-    const int koff = j * (2 * D) + 16 * g;  // K row base + j, dims 8g.. of each 32-dim step
-    const int voff = lane * 16;             // V tile as contiguous 16-byte chunks
+    // K in the A-operand layout (row j, dims 8g.. of each 32-dim step: one
+    // table lookup per lane; contiguous chunks measured 0.2 us slower here),
+    // V as contiguous 16-byte chunks
+    const int koff = j * (2 * D) + 16 * g;
+    const int voff = lane * 16;
     const uint16_t* knew = reinterpret_cast<const uint16_t*>(a.k_new) + ((size_t)b * a.n_kv_heads + kvg) * D;
     const uint16_t* vnew = reinterpret_cast<const uint16_t*>(a.v_new) + ((size_t)b * a.n_kv_heads + kvg) * D;
 
@@ -960,9 +1003,16 @@ struct MfmaPiece {
     const int TB = b_first < b_re ? (b_re - b_first + stride - 1) / stride : 0;
     const int total = TA + TB;
 
-    const int koff = j * (2 * D) + 16 * g;  // K row base + j, dims 8g.. of each 32-dim step
-    const int voff = lane * 16;             // V tile as contiguous 16-byte chunks
+    const int voff = lane * 16;  // V tiles as contiguous 16-byte chunks
     unsigned char* vs = sm.u.t.v[wave];
+    unsigned char* ks = sm.u.t.k[wave];
+    // K chunk i of this lane: contiguous as V (kStageK), else in the A-operand
+    // layout (row j, dims [32 i + 8 g, 32 i + 8 g + 8)); its row in the tile,
+    // its first dim, and its byte offset koff + kstep i in the tile
+    auto krow = [&](int i) { return kStageK ? (i * 64 + lane) / CPR : j; };
+    auto kdim = [&](int i) { return kStageK ? 8 * ((i * 64 + lane) % CPR) : 32 * i + 8 * g; };
+    const int koff = kStageK ? voff : j * (2 * D) + 16 * g;
+    constexpr int kstep = kStageK ? 1024 : 64;
 
     // Rows [base, base + TR) of tile t. Buffer resources span exactly the rows
     // [0, cache) of the piece's (sequence, kv head); loads past them (the tail
@@ -982,8 +1032,8 @@ struct MfmaPiece {
           buffer_rsrc(reinterpret_cast<const uint16_t*>(a.v) + row0 * D, rows * (2 * D));
       const int kb = base * (2 * D) + koff;
 #pragma unroll
-      for (int k = 0; k < KS; ++k)
-        kr[k] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(kres, kb + 64 * k, 0, kStreamLoad));
+      for (int i = 0; i < KS; ++i)
+        kr[i] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(kres, kb + kstep * i, 0, kStreamLoad));
       const int vb = base * (2 * D) + voff;
 #pragma unroll
       for (int i = 0; i < VCH; ++i) vr[i] = __builtin_amdgcn_raw_buffer_load_b128(vres, vb + 1024 * i, 0, kStreamLoad);
@@ -991,9 +1041,9 @@ struct MfmaPiece {
         const size_t src = ((size_t)sb * a.n_kv_heads + skvg) * D;
         const uint16_t* knew = reinterpret_cast<const uint16_t*>(a.k_new) + src;
         const uint16_t* vnew = reinterpret_cast<const uint16_t*>(a.v_new) + src;
-        if (base + j == fresh) {
 #pragma unroll
-          for (int k = 0; k < KS; ++k) kr[k] = *reinterpret_cast<const bf16x8_t*>(knew + 32 * k + 8 * g);
+        for (int i = 0; i < KS; ++i) {
+          if (base + krow(i) == fresh) kr[i] = *reinterpret_cast<const bf16x8_t*>(knew + kdim(i));
         }
 #pragma unroll
         for (int i = 0; i < VCH; ++i) {
@@ -1034,20 +1084,21 @@ struct MfmaPiece {
       const int base = inA ? a_first + t * stride : b_first + (t - TA) * stride;
       const int r_end = inA ? a_re : b_re;
       const int fresh = inA ? a_fresh : b_fresh;
-      // stage V row-major in LDS
+      // stage V and K row-major in LDS
 #pragma unroll
       for (int i = 0; i < VCH; ++i) {
         const int f = i * 64 + lane;
         *reinterpret_cast<u32x4_t*>(vs + (f / CPR) * VSTRIDE + (f % CPR) * 16) = vr[i];
       }
+      if constexpr (kStageK) stage_k(ks, kr);
       if (fresh >= base && fresh < base + TR && (inA ? A.chunk : Bp.chunk) == 0) {
         const int sb = inA ? a_b : b_b, skvg = inA ? a_kvg : b_kvg;
         const size_t row = ((size_t)sb * a.n_kv_heads + skvg) * (size_t)a.max_context + fresh;
         uint16_t* kd = reinterpret_cast<uint16_t*>(const_cast<void*>(a.k)) + row * D;
         uint16_t* vd = reinterpret_cast<uint16_t*>(const_cast<void*>(a.v)) + row * D;
-        if (base + j == fresh) {
 #pragma unroll
-          for (int k = 0; k < KS; ++k) *reinterpret_cast<bf16x8_t*>(kd + 32 * k + 8 * g) = kr[k];
+        for (int i = 0; i < KS; ++i) {
+          if (base + krow(i) == fresh) *reinterpret_cast<bf16x8_t*>(kd + kdim(i)) = kr[i];
         }
 #pragma unroll
         for (int i = 0; i < VCH; ++i) {
@@ -1057,8 +1108,12 @@ struct MfmaPiece {
       }
       // scores: s[u] = K[row base + 4g + u] . q[head column j]
       f32x4_t s = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      if constexpr (kStageK) {
+        s = scores(ks, qa);
+      } else {
 #pragma unroll
-      for (int k = 0; k < KS; ++k) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[k], qa[k], s, 0, 0, 0);
+        for (int k = 0; k < KS; ++k) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[k], qa[k], s, 0, 0, 0);
+      }
       if (base + TR > r_end) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) s[u] = (base + 4 * g + u < r_end) ? s[u] : -INFINITY;
@@ -1251,6 +1306,13 @@ struct I8Piece {
   static constexpr int KL = D / 64;           // K code vectors per lane per tile (D / 4 codes)
   static constexpr int VL = TR * CPR / 64;    // V code vectors per lane per tile
   static constexpr int VSTRIDE = Base::VSTRIDE;
+  // K code tiles staged through LDS where a row is wider than 64 bytes (see
+  // MfmaPiece::stage_k), and the bytes per staged K code row (in the bf16
+  // piece's K area, which is larger); the skew spreads the 16 rows of an
+  // A-operand read over the banks
+  static constexpr bool kStageK = D > 64;
+  static constexpr int KSTRIDE = D + 16;
+  static_assert(!kStageK || (Base::kStageK && KSTRIDE <= Base::KSTRIDE), "K codes fit the K staging area");
   static constexpr int NBUF = Base::NBUF;  // (three tiles measured the same, four slower)
   // Two workgroups per CU where the registers allow (d_h <= 128): the int8
   // tile's conversions make each wave's chain long enough that a second
@@ -1312,14 +1374,21 @@ struct I8Piece {
       if (wave < 2) quantize_new_row(a, sm, b, kvg, wave);
       __syncthreads();
     }
-    const int koff = j * D + g * (D / 4);  // row j, this lane's quarter of the dims
-    const int voff = lane * 16;            // V tile as contiguous 16-byte vectors
+    // V code tiles as contiguous 16-byte vectors; K code vector i of this
+    // lane: contiguous too with kStageK (staged in LDS and read back in the
+    // A-operand layout, as in the bf16 piece), else row j's codes
+    // [g D/4 + 16 i, g D/4 + 16 i + 16). krow: its row in the tile; kcol: its
+    // first code.
+    const int voff = lane * 16;
     unsigned char* vs = sm.u.t.v[wave];
+    unsigned char* ks = sm.u.t.k[wave];
+    auto krow = [&](int i) { return kStageK ? (i * 64 + lane) / CPR : j; };
+    auto kcol = [&](int i) { return kStageK ? 16 * ((i * 64 + lane) % CPR) : g * (D / 4) + 16 * i; };
 
     auto load_tile = [&](int base, Tile& tl) {
-      const int kb = base * D + koff;
 #pragma unroll
-      for (int i = 0; i < KL; ++i) tl.k[i] = __builtin_amdgcn_raw_buffer_load_b128(kres, kb + 16 * i, 0, kStreamLoad);
+      for (int i = 0; i < KL; ++i)
+        tl.k[i] = __builtin_amdgcn_raw_buffer_load_b128(kres, (base + krow(i)) * D + kcol(i), 0, kStreamLoad);
       const int vb = base * D + voff;
 #pragma unroll
       for (int i = 0; i < VL; ++i) tl.v[i] = __builtin_amdgcn_raw_buffer_load_b128(vres, vb + 1024 * i, 0, kStreamLoad);
@@ -1330,9 +1399,9 @@ struct I8Piece {
       constexpr bool kPatch = decltype(patch_tag)::value;  // the piece holds the new row
       Tile tl = tile;
       if (kPatch && fresh >= base && fresh < base + TR) {  // this tile holds the new row
-        if (base + j == fresh) {
 #pragma unroll
-          for (int i = 0; i < KL; ++i) tl.k[i] = *reinterpret_cast<const u32x4_t*>(sm.nq[0] + g * (D / 4) + 16 * i);
+        for (int i = 0; i < KL; ++i) {
+          if (base + krow(i) == fresh) tl.k[i] = *reinterpret_cast<const u32x4_t*>(sm.nq[0] + kcol(i));
         }
 #pragma unroll
         for (int i = 0; i < VL; ++i) {
@@ -1357,12 +1426,26 @@ struct I8Piece {
         *reinterpret_cast<u32x4_t*>(dst) = lo;
         *reinterpret_cast<u32x4_t*>(dst + 16) = hi;
       }
+      // K codes in the A-operand layout (row j's codes [g D/4, (g + 1) D/4)):
+      // with kStageK, staged row-major and read back
+      u32x4_t kc[KL];
+      if constexpr (kStageK) {
+#pragma unroll
+        for (int i = 0; i < KL; ++i)
+          *reinterpret_cast<u32x4_t*>(ks + krow(i) * KSTRIDE + kcol(i)) = tl.k[i];
+#pragma unroll
+        for (int i = 0; i < KL; ++i)
+          kc[i] = *reinterpret_cast<const u32x4_t*>(ks + j * KSTRIDE + g * (D / 4) + 16 * i);
+      } else {
+#pragma unroll
+        for (int i = 0; i < KL; ++i) kc[i] = tl.k[i];
+      }
       // scores: codes . q on the matrix cores, then the rows' K scales
       f32x4_t sc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int i = 0; i < KL; ++i) {
         u32x4_t lo, hi;
-        codes_to_bf16(tl.k[i], lo, hi);
+        codes_to_bf16(kc[i], lo, hi);
         sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, lo), qb[2 * i], sc, 0, 0, 0);
         sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, hi), qb[2 * i + 1], sc, 0, 0, 0);
       }
