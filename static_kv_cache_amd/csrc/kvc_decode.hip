@@ -11,7 +11,7 @@
 // How (flash-decoding style, exact up to rounding order):
 //  - Work space. A "segment" is the valid rows [0, n_b) of one (sequence,
 //    kv head, head chunk); segments are laid end to end in one row space
-//    (each with a fixed number of start-up rows in front, see kSegRows).
+//    (each with a fixed number of start-up rows in front, P::kSegRows).
 //    The grid is persistent: one 256-thread workgroup per CU by default, and
 //    the workgroups take consecutive equal ranges of that space (stream-K
 //    style), so every workgroup streams about the same number of rows
@@ -187,9 +187,8 @@ __device__ __forceinline__ void fused_write(const DecodeArgs& a, int b, int g, i
 // the number of rows. Each segment is given this many virtual rows in front
 // of its real ones, so a workgroup whose range crosses into another segment
 // is handed correspondingly fewer real rows and all workgroups finish
-// together. Virtual rows map to no work.
-constexpr int kSegRows = 192;  // measured (two pieces streamed as one): 0 / 64 / 128 / 192 / 256 -> 33.9 / 32.9 / 32.5 / 32.4 / 32.6 us
-static_assert(kSegRows >= 0 && kSegRows <= kMaxSegRows, "row space must stay below 2^31");
+// together. Virtual rows map to no work. The allowance is the piece's
+// (P::kSegRows), measured per piece at the Llama-3 shape.
 
 
 // A piece that is part of a segment (only a workgroup's first and last
@@ -430,6 +429,7 @@ struct ValuPiece {
 
   // Rows [r_begin, r_end) of segment (b, g, chunk). Writes the normalised
   // output when the piece is the whole segment, else the partial of `slot`.
+  static constexpr int kSegRows = 192;  // start-up rows of a segment (see the row space)
   static constexpr bool kSpeculative = true;  // nothing but shared memory is touched before the gate
   static constexpr bool kPair = false;
   struct PieceRef {};
@@ -695,6 +695,12 @@ struct MfmaPiece {
   // One workgroup per CU: measured faster than the two a CU could hold (fewer
   // pieces to merge, no second workgroup competing for issue slots and LDS).
   static constexpr int kWgPerCu = 1;
+  // Start-up rows of a segment (see the row space). Llama-3 layer step at
+  // 192 / 224 / 256 start-up rows: 32.17 / 31.74 / 31.95 us on one machine,
+  // 224 / 256 / 288: 31.48 / 31.75 / 31.70 on a second, 192 / 256 / 320:
+  // 31.65 / 31.18 / 31.44 on a third; long context 29.15 / 29.13 / 29.64
+  // at 192 / 224 / 256.
+  static constexpr int kSegRows = 224;
 
   // With kStageK, K tiles are loaded like V tiles, as contiguous 16-byte
   // chunks (chunk i of lane l is chunk f % CPR of row f / CPR, f = 64 i + l),
@@ -1334,6 +1340,8 @@ struct I8Piece {
 
   static constexpr bool kSpeculative = true;  // nothing but shared memory is touched before the gate
   static constexpr bool kPair = false;
+  // start-up rows of a segment: 192 / 224 / 256 -> decode 22.52 / 22.42 / 21.74 us
+  static constexpr int kSegRows = 256;
   struct PieceRef {};
   static __device__ __forceinline__ bool run(const DecodeArgs& a, Smem& sm, int b, int kvg, int chunk,
                                              int r_begin, int r_end, int n, bool whole, long long slot,
@@ -1576,6 +1584,7 @@ struct I8Piece {
 // Persistent decode kernel: grid = W workgroups of 256 threads.
 template <class P>
 __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(DecodeArgs a) {
+  static_assert(P::kSegRows >= 0 && P::kSegRows <= kMaxSegRows, "row space must stay below 2^31");
   __shared__ typename P::Smem sm;
   __shared__ int32_t s_prefix[KVC_MAX_BATCH + 1];
   __shared__ int32_t s_umax;  // longest segment in virtual rows
@@ -1605,7 +1614,7 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(DecodeArgs a) {
     second[i] = entry[1 + kPieceInts + i];
   }
   if (t < 64) {
-    scan_lengths(a.valid_lens, a.cache_index, B, a.max_context, kSegRows, s_prefix, &s_umax, a.err_flag,
+    scan_lengths(a.valid_lens, a.cache_index, B, a.max_context, P::kSegRows, s_prefix, &s_umax, a.err_flag,
                  blockIdx.x == 0, min_rows, a.plan + KVC_PLAN_LENS, &st.gate);
     if (t == 0) st.gate = st.gate && key;
   }
@@ -1711,7 +1720,7 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(DecodeArgs a) {
   // merged. A split then costs more (partial stores, count-in, merge) than
   // it saves on so few rows.
   const int nseg = B * HC;
-  const bool whole_mode = nseg <= a.n_wg && s_umax - kSegRows <= a.whole_rows;
+  const bool whole_mode = nseg <= a.n_wg && s_umax - P::kSegRows <= a.whole_rows;
   int recorded = 0;  // pieces in this workgroup's new entry (thread 0)
   if (w < (whole_mode ? nseg : part.W)) {
     long long x, hi;
@@ -1724,7 +1733,7 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(DecodeArgs a) {
       x = part.lo(w);
       hi = part.lo(w + 1);
     }
-    if (x < hi) for_each_piece(s_prefix, B, HC, kSegRows, x, hi,
+    if (x < hi) for_each_piece(s_prefix, B, HC, P::kSegRows, x, hi,
                    [&](int b, int hc, int r_begin, int r_end, int n, long long real0) {
       const long long s = (long long)b * HC + hc;
       const bool whole = r_begin == 0 && r_end == n;
@@ -1748,7 +1757,7 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(DecodeArgs a) {
     });
     if (nsplit > 0) finish_splits<typename P::Elem, P::kD, P::kSlotHeads>(a, split, nsplit, s_flag);
   }
-  if (fresh) plan_publish(a.plan, st, recorded, s_prefix, B, kSegRows, a.n_wg, plan_mode);
+  if (fresh) plan_publish(a.plan, st, recorded, s_prefix, B, P::kSegRows, a.n_wg, plan_mode);
 }
 
 template <class P, typename T, int D>
