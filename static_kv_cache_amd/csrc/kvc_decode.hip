@@ -1340,8 +1340,13 @@ struct I8Piece {
 
   static constexpr bool kSpeculative = true;  // nothing but shared memory is touched before the gate
   static constexpr bool kPair = false;
-  // start-up rows of a segment: 192 / 224 / 256 -> decode 22.52 / 22.42 / 21.74 us
-  static constexpr int kSegRows = 256;
+  // Start-up rows of a segment. Decode alone, 192 / 224 / 256 / 384 / 448 /
+  // 512: 22.52 / 22.42 / 21.74 / 21.80 / 21.79 / 22.06 us; the fused layer
+  // step (its piece holding the new row quantises it behind a barrier
+  // before its tiles), 256 / 384 / 448 / 512: 23.43 / 22.49 / 22.07 / 21.94.
+  // One value serves both modes, so that a fused launch and append + decode
+  // split the rows alike and give the same bits.
+  static constexpr int kSegRows = 448;
   struct PieceRef {};
   static __device__ __forceinline__ bool run(const DecodeArgs& a, Smem& sm, int b, int kvg, int chunk,
                                              int r_begin, int r_end, int n, bool whole, long long slot,
