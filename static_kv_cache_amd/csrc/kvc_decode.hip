@@ -1599,16 +1599,7 @@ __global__ __launch_bounds__(kThreads) void gqa_decode_kernel(DecodeArgs a) {
 
   const int B = a.batch;
   const int t = threadIdx.x;
-  // XCD-major row ranges: workgroups are handed to the 8 XCDs in turn
-  // (workgroup b to XCD b mod 8), and each XCD takes one contiguous eighth of
-  // the row space (b -> (b mod 8) W/8 + b/8), so the pieces of one segment
-  // share an XCD. With one workgroup per CU: layer step 31.36 -> 31.25 us,
-  // the same layer from the Infinity Cache 29.7 -> 29.1, long context 29.1 ->
-  // 28.8; the int8 piece (two per CU) lost 0.3 us in its layer step and keeps
-  // the plain order. Any bijection gives correct results.
-  constexpr bool kXcdMajor = P::kWgPerCu == 1;
-  const int w = (kXcdMajor && a.n_wg % 8 == 0) ? (int)(blockIdx.x % 8) * (a.n_wg / 8) + (int)(blockIdx.x / 8)
-                                               : (int)blockIdx.x;
+  const int w = blockIdx.x;
   const int min_rows = a.k_new ? 1 : 0;
   const int HC = a.n_kv_heads * a.head_chunks;  // segments per sequence
   const int32_t* entry = plan_entry(a.plan);
